@@ -1,0 +1,254 @@
+"""CPU oracle of the MaskLLM differentiable N:M mask path.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The product path
+(the ``sparsity_masks_weights_amd`` package and its HIP library) never imports,
+links or calls it, and shares no code with it.
+
+The arithmetic lives in ``maskgs_oracle.c`` (plain C, fp64 apart from the fp32
+noise contract described there); this module only builds that file with gcc and
+marshals numpy arrays into it.  Every function cites the passage of the MaskLLM
+summary page ("MaskLLM: Learnable Semi-Structured Sparsity for Large Language
+Models", paper-graph-ui summary of arXiv 2409.17481) that it follows.
+
+Parity pins of this oracle live in ``tests/test_oracle_*.py``.  Parity unpinned
+(self-consistent definitions the pages do not fix): the choice of Philox word
+layout, of the uniform map and of the contract logarithm's coefficients.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "maskgs_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+NO_NOISE = 1
+EXACT_LOGITS = 2
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc (always recompiles).  Returns the .so path."""
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-shared",
+           "-fPIC", "-std=c11", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    L = ctypes.CDLL(_LIB)
+    c = ctypes
+    P = c.c_void_p
+    L.orc_set_threads.argtypes = [c.c_int]
+    L.orc_get_threads.restype = c.c_int
+    L.orc_candidates.argtypes = [c.c_int, c.c_int, P, c.c_int]
+    L.orc_candidates.restype = c.c_int
+    L.orc_philox4x32_10.argtypes = [P, P, P]
+    L.orc_philox_word.argtypes = [c.c_uint64, c.c_uint32, c.c_uint32, c.c_uint64]
+    L.orc_philox_word.restype = c.c_uint32
+    L.orc_philox_words.argtypes = [c.c_uint64, c.c_uint32, c.c_uint32, c.c_uint64, c.c_int64, P]
+    L.orc_uniform.argtypes = [c.c_uint32]
+    L.orc_uniform.restype = c.c_float
+    L.orc_ln_contract.argtypes = [c.c_float]
+    L.orc_ln_contract.restype = c.c_float
+    L.orc_gumbel.argtypes = [c.c_uint32]
+    L.orc_gumbel.restype = c.c_float
+    L.orc_gumbel_all.argtypes = [P]
+    L.orc_bf16_from_double.argtypes = [c.c_double]
+    L.orc_bf16_from_double.restype = c.c_uint16
+    common = [c.c_int, c.c_int, c.c_int64, c.c_int64, c.c_uint64, c.c_uint32,
+              c.c_uint64, c.c_uint32, c.c_float, c.c_float, c.c_uint32]
+    L.orc_fwd.argtypes = common + [P, P, P, P, P, P, P]
+    L.orc_fwd.restype = c.c_int
+    L.orc_bwd.argtypes = common + [P, P, P, c.c_double, P, P]
+    L.orc_bwd.restype = c.c_int
+    L.orc_hard_extract.argtypes = [c.c_int, c.c_int, c.c_int64, c.c_int64, P, P, c.c_int,
+                                   P, P, P, P]
+    L.orc_hard_extract.restype = c.c_int
+    L.orc_magnitude_mask.argtypes = [c.c_int, c.c_int, c.c_int64, c.c_int64, P, P]
+    L.orc_magnitude_mask.restype = c.c_int
+    L.orc_prior_init.argtypes = [c.c_int, c.c_int, c.c_int64, c.c_int64, P, P, P,
+                                 c.c_float, c.c_int]
+    L.orc_prior_init.restype = c.c_int
+    _lib = L
+    return L
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def widen_bf16(u16: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> the same values as fp32 (exact)."""
+    u = np.ascontiguousarray(u16, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32)
+
+
+def set_threads(t: int) -> None:
+    lib().orc_set_threads(int(t))
+
+
+def get_threads() -> int:
+    return int(lib().orc_get_threads())
+
+
+def candidates(n: int, m: int) -> np.ndarray:
+    """Candidate masks S as uint8 bitmasks (bit j = keep position j)."""
+    buf = np.zeros(128, dtype=np.uint8)
+    k = lib().orc_candidates(n, m, _ptr(buf), 128)
+    if k < 0:
+        raise ValueError(f"invalid N:M {n}:{m}")
+    return buf[:k].copy()
+
+
+def candidate_matrix(n: int, m: int) -> np.ndarray:
+    """S as a {0,1} matrix of shape [K, M] (section 3.4, Eq. 7)."""
+    c = candidates(n, m)
+    return ((c[:, None] >> np.arange(m)[None, :]) & 1).astype(np.int64)
+
+
+def philox4x32_10(counter, key) -> np.ndarray:
+    ctr = np.ascontiguousarray(counter, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    lib().orc_philox4x32_10(_ptr(ctr), _ptr(k), _ptr(out))
+    return out
+
+
+def philox_words(seed: int, step: int, tensor_id: int, n0: int, count: int) -> np.ndarray:
+    out = np.zeros(count, dtype=np.uint32)
+    lib().orc_philox_words(seed, step, tensor_id, n0, count, _ptr(out))
+    return out
+
+
+def uniform(x: int) -> float:
+    return float(lib().orc_uniform(int(x)))
+
+
+def ln_contract(x: float) -> float:
+    return float(lib().orc_ln_contract(float(x)))
+
+
+def gumbel(x: int) -> float:
+    return float(lib().orc_gumbel(int(x)))
+
+
+def gumbel_all() -> np.ndarray:
+    """g for all 2^23 uniforms, indexed by x >> 9."""
+    out = np.zeros(1 << 23, dtype=np.float32)
+    lib().orc_gumbel_all(_ptr(out))
+    return out
+
+
+def bf16_from_double(v: float) -> int:
+    return int(lib().orc_bf16_from_double(float(v)))
+
+
+def fwd(n, m, w, z, *, kappa, tau, seed=0, step=0, tensor_id=0, block_offset=0, flags=0,
+        out_dtype="bf16"):
+    """Forward of the mask path on a [rows, cols] weight.
+
+    Returns dict(y=[B,K] f64, m=[B,M] f64, out=[rows,cols] (uint16 bf16 bits or
+    f32), reg=float).  w is fp32 (widen bf16 first), z is fp32 [B, K].
+    """
+    w = _f32(w)
+    rows, cols = w.shape
+    B = rows * (cols // m)
+    K = len(candidates(n, m))
+    z = _f32(z).reshape(B, K)
+    y = np.zeros((B, K), dtype=np.float64)
+    mk = np.zeros((B, m), dtype=np.float64)
+    reg = ctypes.c_double(0.0)
+    out16 = np.zeros((rows, cols), dtype=np.uint16) if out_dtype == "bf16" else None
+    out32 = np.zeros((rows, cols), dtype=np.float32) if out_dtype == "f32" else None
+    rc = lib().orc_fwd(n, m, rows, cols, block_offset, tensor_id, seed, step, kappa, tau, flags,
+                       _ptr(w), _ptr(z), _ptr(y), _ptr(mk), _ptr(out16), _ptr(out32),
+                       ctypes.addressof(reg))
+    if rc != 0:
+        raise ValueError("oracle fwd: invalid arguments")
+    return dict(y=y, m=mk, out=out16 if out16 is not None else out32, reg=reg.value)
+
+
+def bwd(n, m, w, z, g_up, *, kappa, tau, lam, seed=0, step=0, tensor_id=0, block_offset=0,
+        flags=0, dz_prev=None):
+    """Gradient of L_LM - lambda*R with respect to the logits, [B, K] f64."""
+    w = _f32(w)
+    rows, cols = w.shape
+    B = rows * (cols // m)
+    K = len(candidates(n, m))
+    z = _f32(z).reshape(B, K)
+    g_up = _f32(g_up).reshape(rows, cols)
+    prev = None if dz_prev is None else _f32(dz_prev).reshape(B, K)
+    dz = np.zeros((B, K), dtype=np.float64)
+    rc = lib().orc_bwd(n, m, rows, cols, block_offset, tensor_id, seed, step, kappa, tau, flags,
+                       _ptr(w), _ptr(z), _ptr(g_up), float(lam), _ptr(prev), _ptr(dz))
+    if rc != 0:
+        raise ValueError("oracle bwd: invalid arguments")
+    return dz
+
+
+def hard_extract(n, m, z, rows, cols, w_raw=None):
+    """Argmax index, packed bits and (2:4) compacted values / 2-bit indices.
+
+    w_raw: the weight as stored (uint16 bf16 bits or float32), [rows, cols].
+    """
+    B = rows * (cols // m)
+    K = len(candidates(n, m))
+    z = _f32(z).reshape(B, K)
+    idx = np.zeros(B, dtype=np.uint8)
+    bits = np.zeros((B * m + 7) // 8, dtype=np.uint8)
+    values = val_idx = None
+    wb = 0
+    if w_raw is not None:
+        w_raw = np.ascontiguousarray(w_raw)
+        wb = w_raw.dtype.itemsize
+        values = np.zeros(B * n, dtype=w_raw.dtype)
+        val_idx = np.zeros((B + 1) // 2, dtype=np.uint8)
+    rc = lib().orc_hard_extract(n, m, rows, cols, _ptr(z), _ptr(w_raw), wb, _ptr(idx),
+                                _ptr(bits), _ptr(values), _ptr(val_idx))
+    if rc != 0:
+        raise ValueError(f"oracle hard_extract: rc={rc}")
+    return dict(idx=idx, bits=bits, values=values, val_idx=val_idx)
+
+
+def magnitude_mask(n, m, w):
+    w = _f32(w)
+    rows, cols = w.shape
+    B = rows * (cols // m)
+    bits = np.zeros((B * m + 7) // 8, dtype=np.uint8)
+    if lib().orc_magnitude_mask(n, m, rows, cols, _ptr(w), _ptr(bits)) != 0:
+        raise ValueError("oracle magnitude_mask: invalid arguments")
+    return bits
+
+
+def prior_init(n, m, z, rows, cols, *, alpha, mode=0, prior_bits=None, w=None):
+    """Eq. 9-10 prior seeding; returns a new fp32 [B, K] array."""
+    B = rows * (cols // m)
+    K = len(candidates(n, m))
+    zz = _f32(z).reshape(B, K).copy()
+    pb = None if prior_bits is None else np.ascontiguousarray(prior_bits, dtype=np.uint8)
+    ww = None if w is None else _f32(w)
+    if pb is None and ww is None:
+        raise ValueError("prior_init needs prior_bits or w")
+    rc = lib().orc_prior_init(n, m, rows, cols, _ptr(zz), _ptr(pb), _ptr(ww), float(alpha),
+                              int(mode))
+    if rc != 0:
+        raise ValueError(f"oracle prior_init: rc={rc}")
+    return zz
