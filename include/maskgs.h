@@ -1,0 +1,184 @@
+/*
+ * maskgs.h -- C ABI of libmaskgs: the differentiable N:M mask path of MaskLLM
+ * ("MaskLLM: Learnable Semi-Structured Sparsity for Large Language Models",
+ * arXiv 2409.17481; citations below name sections of its paper-graph-ui
+ * summary page) on AMD Instinct MI355X (gfx950).
+ *
+ * Every block of M consecutive weights of a frozen weight matrix carries K =
+ * C(M,N) learnable fp32 logits z (one per candidate N:M mask).  The library
+ * draws Gumbel noise for every (block, candidate) from a counter-based Philox
+ * stream, forms the soft index y = softmax((kappa*z + g)/tau), the soft mask
+ * M~ = y.S and W (.) M~; it maps the upstream gradient plus the sparse-weight
+ * regulariser back to dL/dz; it extracts, packs and compacts the hard mask
+ * argmax(z); and it seeds logits from a prior mask.
+ *
+ * Conventions shared by all entry points
+ *   Layout.   W, W(.)M~ and the upstream gradient are row-major [rows, cols];
+ *             block b = r*(cols/M) + c covers W[r, c*M .. c*M+M-1] (blocks run
+ *             along the contiguous, input dimension).  Logits, soft indices and
+ *             logit gradients are fp32 [B, K] with K innermost, B = rows*cols/M.
+ *   Support.  N:M = 2:4 (K = 6) and 4:8 (K = 70) on the GPU.
+ *   Memory.   Every array argument is device memory owned by the caller, except
+ *             where a comment says "host".  The library allocates nothing and
+ *             keeps no mutable state between calls; calls are thread safe.
+ *             Every device pointer must be 16-byte aligned.  Outputs must not
+ *             alias inputs except where stated (prior_init updates z in place,
+ *             bwd with accumulate reads and writes dz).
+ *   Streams.  Work is enqueued on the given HIP stream (0 = null stream) and
+ *             runs asynchronously; faults surface at the caller's synchronise.
+ *   Errors.   Each call returns MASKGS_OK (0) or a MASKGS_E_* status.  All
+ *             argument checks run on the host before anything is enqueued: on
+ *             an error status nothing has been launched.  Data-dependent
+ *             conditions (NaN logits, priors matching no candidate) are not
+ *             errors; their behaviour is stated per entry point.
+ */
+#ifndef MASKGS_H
+#define MASKGS_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MASKGS_ABI_VERSION 1
+
+/* Status codes. */
+#define MASKGS_OK 0
+#define MASKGS_E_NULL 1        /* a required pointer is NULL                      */
+#define MASKGS_E_SHAPE 2       /* rows/cols negative, or cols % M != 0            */
+#define MASKGS_E_UNSUPPORTED 3 /* N:M other than 2:4 / 4:8, or 2:4-only output    */
+#define MASKGS_E_DTYPE 4       /* dtype code out of range                         */
+#define MASKGS_E_ALIGN 5       /* a device pointer is not 16-byte aligned         */
+#define MASKGS_E_RANGE 6       /* kappa<=0, tau<=0, lambda<0, alpha<0, non-finite, bad mode */
+#define MASKGS_E_HIP 7         /* the HIP runtime refused a launch                */
+#define MASKGS_E_CAPACITY 8    /* a host output buffer is too small               */
+
+/* Element types of weights, masked weights and upstream gradients. */
+typedef enum { MASKGS_F32 = 0, MASKGS_BF16 = 1 } maskgs_dtype;
+
+/* Sample flags. */
+#define MASKGS_NO_NOISE 1u /* g = 0 for every candidate (tests and diagnostics) */
+
+/* One weight tensor (or a row range of one).  block_offset is the global index
+ * of the first block described: the noise of a block depends on its global
+ * index, so a tensor split into row ranges with matching offsets draws exactly
+ * the noise of the whole tensor.  tensor_id separates the noise streams of the
+ * layers of a model. */
+typedef struct {
+    int32_t n, m;          /* N:M pattern: keep n of every m weights             */
+    int64_t rows, cols;    /* weight shape [rows, cols]                          */
+    uint64_t block_offset; /* global index of block 0 of this call               */
+    uint32_t tensor_id;    /* noise stream of this tensor                        */
+} maskgs_tensor_desc;
+
+/* One draw of the Gumbel soft index.  The Philox4x32-10 stream (Salmon et al.,
+ * SC'11) gives word n = global_block*K + candidate as output n%4 of the call
+ * with counter (lo32(n/4), hi32(n/4), step, tensor_id) and key (lo32(seed),
+ * hi32(seed)).  kappa and tau follow the schedules of section 3.4 (kappa
+ * 100 -> 500, tau 4 -> 0.05); the caller evaluates the schedule per step. */
+typedef struct {
+    uint64_t seed;
+    uint32_t step;
+    float kappa; /* logit scale, > 0 (section 3.4, logit parameterisation)  */
+    float tau;   /* temperature, > 0 (section 3.4, Eq. 6)                   */
+    uint32_t flags;
+} maskgs_sample_params;
+
+/* Library version of this header's ABI (MASKGS_ABI_VERSION). */
+int maskgs_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char *maskgs_status_str(int status);
+
+/* Candidate masks S (section 3.2 candidate set; section 3.4 Eq. 7).  Writes the
+ * K = C(m,n) masks to masks_host (HOST memory, capacity entries) as bitmasks,
+ * bit j set = keep position j.  Order: for 2:4 the order in which the page
+ * lists the six patterns ([1,1,0,0],[1,0,1,0],[1,0,0,1],[0,1,0,1],[0,1,1,0],
+ * [0,0,1,1], first position = bit 0); for 4:8 lexicographic order of the sorted
+ * kept positions.  *k_out = K (may be NULL).  E_UNSUPPORTED for other N:M,
+ * E_CAPACITY if capacity < K (nothing written). */
+int maskgs_candidates(int32_t n, int32_t m, uint8_t *masks_host, int32_t capacity, int32_t *k_out);
+
+/* Forward of the mask path (section 3.4, Eqs. 5-7 and Algorithm 1; section 3.2
+ * frozen backbone).  Per block: g_i Gumbel noise (Eq. 5), a_i =
+ * fp32(fp32(kappa*z_i + g_i) * fp32(1/tau)), y = softmax(a) (Eq. 6),
+ * m = y.S (Eq. 7), out = W (.) m.
+ *   w        [rows, cols] of w_dt, frozen weight.
+ *   z        [B, K] fp32 logits.
+ *   out      [rows, cols] of out_dt: W (.) M~ (bf16: round to nearest even).
+ *   y_save   NULL, or [B, K] fp32: the soft index, for maskgs_bwd.
+ *   reg_accum NULL, or ONE device double to which sum_b ||W_b (.) M~_b||^2 is
+ *            added atomically (the regulariser value R of Eq. 8; the loss term
+ *            is -lambda*R).  The caller zeroes it.
+ * NaN logits propagate to y, out and R. */
+int maskgs_fwd(const maskgs_tensor_desc *t, const maskgs_sample_params *p, const void *w,
+               maskgs_dtype w_dt, const float *z, void *out, maskgs_dtype out_dt, float *y_save,
+               double *reg_accum, hipStream_t stream);
+
+/* Backward to the logits (section 3.2 information flow; section 3.4 Eq. 8).
+ * With G = dL_LM/d(W (.) M~) and W frozen, the gradient of
+ * L = L_LM - lambda * sum_b ||W_b (.) M~_b||^2 is, per block,
+ *   dm_j = G_j w_j - 2 lambda w_j^2 m_j,   dy_i = sum_j S_ij dm_j,
+ *   dz_i = (kappa/tau) y_i (dy_i - sum_k y_k dy_k).
+ *   y_saved  NULL (recompute y from z with the same seed/step: bit-identical to
+ *            the forward's), or the y_save written by maskgs_fwd.
+ *   z        [B, K]; may be NULL when y_saved is given.
+ *   dout     [rows, cols] of dout_dt, G.
+ *   dz       [B, K] fp32 output; accumulate != 0 adds to its contents. */
+int maskgs_bwd(const maskgs_tensor_desc *t, const maskgs_sample_params *p, const void *w,
+               maskgs_dtype w_dt, const float *z, const float *y_saved, const void *dout,
+               maskgs_dtype dout_dt, float lambda, float *dz, int32_t accumulate,
+               hipStream_t stream);
+
+/* Regulariser value alone (section 3.4, Eq. 8): adds sum_b ||W_b (.) M~_b||^2 to
+ * *reg_accum (one device double, atomically) without writing W (.) M~.
+ * y_saved as in maskgs_bwd. */
+int maskgs_reg_reduce(const maskgs_tensor_desc *t, const maskgs_sample_params *p, const void *w,
+                      maskgs_dtype w_dt, const float *z, const float *y_saved,
+                      double *reg_accum, hipStream_t stream);
+
+/* Hard mask (section 3.2 inference flow; Algorithm 1 step 3): k_b = the first
+ * index of the largest z_b,i (fp32 compare), M*_b = S_k.  Outputs, each NULL
+ * to skip:
+ *   idx       [B] uint8, k_b.
+ *   mask_bits [ceil(B*m/8)] uint8: M*_b at bits [b*m, b*m+m) of an LSB-first
+ *             bit stream; the unused bits of the last byte are zero.
+ *   values    2:4 only, [B*2] of w_dt: the kept weights of block b in ascending
+ *             position at [2b], [2b+1] (bit copies of w; needs w).
+ *   val_idx   2:4 only, [ceil(B/2)] uint8: nibble p0 | p1<<2 of the two kept
+ *             positions (p0 < p1); block 2i in the low nibble of byte i, block
+ *             2i+1 in the high nibble; the unused high nibble is zero.
+ * block_offset and tensor_id of t are ignored.  A block whose logits are all
+ * NaN selects candidate 0. */
+int maskgs_hard_extract(const maskgs_tensor_desc *t, const float *z, const void *w,
+                        maskgs_dtype w_dt, uint8_t *idx, uint8_t *mask_bits, void *values,
+                        uint8_t *val_idx, hipStream_t stream);
+
+/* Prior seeding (section 3.4, Mask Prior, Eqs. 9-10), z updated in place.
+ * The prior M0 of block b is read from prior_bits (the mask_bits format), or,
+ * when prior_bits is NULL, is the magnitude top-n of w (|w| compared on the
+ * bit pattern with the sign cleared; ties keep the lower position).
+ *   mode 0 (Eq. 10): z_i <- z_i + alpha * sigma_b * sim_i, sim_i = <M0,S_i> -
+ *          mean_k <M0,S_k>, sigma_b the population std of the block's K logits.
+ *   mode 1: z_k0 <- z_k0 + alpha at the candidate S_k0 = M0; a block whose
+ *          prior has no equal candidate is left unchanged.
+ * alpha >= 0 (alpha = 0 leaves z unchanged). */
+int maskgs_prior_init(const maskgs_tensor_desc *t, float *z, const uint8_t *prior_bits,
+                      const void *w, maskgs_dtype w_dt, float alpha, int32_t mode,
+                      hipStream_t stream);
+
+/* Test hooks.  maskgs_debug_philox writes words n0 .. n0+count-1 of the noise
+ * stream of (seed, step, tensor_id) to words (device, count uint32).
+ * maskgs_debug_gumbel maps n Philox words to the fp32 Gumbel noise the forward
+ * uses (device arrays). */
+int maskgs_debug_philox(uint64_t seed, uint32_t step, uint32_t tensor_id, uint64_t n0,
+                        int64_t count, uint32_t *words, hipStream_t stream);
+int maskgs_debug_gumbel(const uint32_t *words, int64_t n, float *g, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MASKGS_H */

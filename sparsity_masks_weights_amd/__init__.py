@@ -1,0 +1,272 @@
+"""libmaskgs: MaskLLM's differentiable N:M mask path on AMD Instinct MI355X.
+
+This package is a thin ctypes binding over the C ABI declared in
+``include/maskgs.h`` (the HIP library ``libmaskgs.so`` built next to this file).
+Every step of the path runs in the library's kernels; Python only marshals
+arguments: it checks tensor device, dtype, shape and contiguity, takes device
+pointers and torch's current HIP stream, and maps status codes to exceptions.
+There is no CPU fallback: without the built library every call raises.
+
+Entry points carry the C names (``maskgs_fwd`` ...).  Citations refer to the
+summary page "MaskLLM: Learnable Semi-Structured Sparsity for Large Language
+Models" (paper-graph-ui summary of arXiv 2409.17481).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmaskgs.so")
+
+MASKGS_OK = 0
+MASKGS_E_NULL = 1
+MASKGS_E_SHAPE = 2
+MASKGS_E_UNSUPPORTED = 3
+MASKGS_E_DTYPE = 4
+MASKGS_E_ALIGN = 5
+MASKGS_E_RANGE = 6
+MASKGS_E_HIP = 7
+MASKGS_E_CAPACITY = 8
+MASKGS_F32 = 0
+MASKGS_BF16 = 1
+MASKGS_NO_NOISE = 1
+
+EXPORTS = ("maskgs_abi_version", "maskgs_status_str", "maskgs_candidates", "maskgs_fwd",
+           "maskgs_bwd", "maskgs_reg_reduce", "maskgs_hard_extract", "maskgs_prior_init",
+           "maskgs_debug_philox", "maskgs_debug_gumbel")
+
+
+class MaskgsError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: status {status} ({msg})")
+        self.status = status
+
+
+class TensorDesc(ctypes.Structure):
+    """maskgs_tensor_desc: N:M, weight shape, global block offset, tensor id."""
+    _fields_ = [("n", ctypes.c_int32), ("m", ctypes.c_int32), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("block_offset", ctypes.c_uint64),
+                ("tensor_id", ctypes.c_uint32)]
+
+
+class SampleParams(ctypes.Structure):
+    """maskgs_sample_params: Philox seed and step, kappa, tau, flags."""
+    _fields_ = [("seed", ctypes.c_uint64), ("step", ctypes.c_uint32), ("kappa", ctypes.c_float),
+                ("tau", ctypes.c_float), ("flags", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmaskgs.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libmaskgs is not built ({path} missing); run "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(path)
+    c = ctypes
+    P = c.c_void_p
+    DP = c.POINTER(TensorDesc)
+    SP = c.POINTER(SampleParams)
+    L.maskgs_abi_version.restype = c.c_int
+    L.maskgs_status_str.argtypes = [c.c_int]
+    L.maskgs_status_str.restype = c.c_char_p
+    L.maskgs_candidates.argtypes = [c.c_int32, c.c_int32, P, c.c_int32, c.POINTER(c.c_int32)]
+    L.maskgs_fwd.argtypes = [DP, SP, P, c.c_int, P, P, c.c_int, P, P, P]
+    L.maskgs_bwd.argtypes = [DP, SP, P, c.c_int, P, P, P, c.c_int, c.c_float, P, c.c_int32, P]
+    L.maskgs_reg_reduce.argtypes = [DP, SP, P, c.c_int, P, P, P, P]
+    L.maskgs_hard_extract.argtypes = [DP, P, P, c.c_int, P, P, P, P, P]
+    L.maskgs_prior_init.argtypes = [DP, P, P, P, c.c_int, c.c_float, c.c_int32, P]
+    L.maskgs_debug_philox.argtypes = [c.c_uint64, c.c_uint32, c.c_uint32, c.c_uint64, c.c_int64,
+                                      P, P]
+    L.maskgs_debug_gumbel.argtypes = [P, c.c_int64, P, P]
+    for name in EXPORTS:
+        if name not in ("maskgs_status_str",):
+            getattr(L, name).restype = c.c_int
+    _lib = L
+    return L
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MASKGS_OK:
+        msg = load_library().maskgs_status_str(status).decode()
+        raise MaskgsError(fn, status, msg)
+
+
+# --------------------------------------------------------------------------
+# Argument marshalling
+# --------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return MASKGS_F32
+    if t.dtype == torch.bfloat16:
+        return MASKGS_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t, name, dtype=None, numel=None, device=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def num_candidates(n: int, m: int) -> int:
+    return {(2, 4): 6, (4, 8): 70}[(n, m)]
+
+
+@dataclass
+class Tensor:
+    """Shape bookkeeping for one masked weight (or a row range of one)."""
+    n: int
+    m: int
+    rows: int
+    cols: int
+    block_offset: int = 0
+    tensor_id: int = 0
+
+    @property
+    def k(self) -> int:
+        return num_candidates(self.n, self.m)
+
+    @property
+    def nblocks(self) -> int:
+        return self.rows * (self.cols // self.m)
+
+    def desc(self) -> TensorDesc:
+        return TensorDesc(self.n, self.m, self.rows, self.cols, self.block_offset, self.tensor_id)
+
+
+def sample_params(seed=0, step=0, kappa=100.0, tau=4.0, flags=0) -> SampleParams:
+    return SampleParams(seed, step, kappa, tau, flags)
+
+
+# --------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# --------------------------------------------------------------------------
+def maskgs_abi_version() -> int:
+    return load_library().maskgs_abi_version()
+
+
+def maskgs_candidates(n: int, m: int) -> list:
+    """Candidate masks S as bitmasks (section 3.2; section 3.4 Eq. 7)."""
+    buf = (ctypes.c_uint8 * 128)()
+    k = ctypes.c_int32(0)
+    _check("maskgs_candidates",
+           load_library().maskgs_candidates(n, m, buf, 128, ctypes.byref(k)))
+    return list(buf[: k.value])
+
+
+def maskgs_fwd(t: Tensor, p: SampleParams, w, z, out, y_save=None, reg_accum=None, stream=None):
+    """W (.) M~ (section 3.4, Eqs. 5-7); optional soft index and regulariser."""
+    dev = w.device
+    _check("maskgs_fwd", load_library().maskgs_fwd(
+        ctypes.byref(t.desc()), ctypes.byref(p),
+        _ptr(w, "w", numel=t.rows * t.cols, device=dev), _dtype_code(w),
+        _ptr(z, "z", _torch().float32, t.nblocks * t.k, dev),
+        _ptr(out, "out", numel=t.rows * t.cols, device=dev), _dtype_code(out),
+        _ptr(y_save, "y_save", _torch().float32, t.nblocks * t.k, dev),
+        _ptr(reg_accum, "reg_accum", _torch().float64, 1, dev), _stream(stream)))
+    return out
+
+
+def maskgs_bwd(t: Tensor, p: SampleParams, w, z, y_saved, dout, lam: float, dz,
+               accumulate: bool = False, stream=None):
+    """dL/dz for L = L_LM - lambda*R (section 3.4 Eq. 8, softmax backward)."""
+    dev = w.device
+    f32 = _torch().float32
+    _check("maskgs_bwd", load_library().maskgs_bwd(
+        ctypes.byref(t.desc()), ctypes.byref(p),
+        _ptr(w, "w", numel=t.rows * t.cols, device=dev), _dtype_code(w),
+        _ptr(z, "z", f32, t.nblocks * t.k, dev),
+        _ptr(y_saved, "y_saved", f32, t.nblocks * t.k, dev),
+        _ptr(dout, "dout", numel=t.rows * t.cols, device=dev), _dtype_code(dout),
+        float(lam), _ptr(dz, "dz", f32, t.nblocks * t.k, dev), int(bool(accumulate)),
+        _stream(stream)))
+    return dz
+
+
+def maskgs_reg_reduce(t: Tensor, p: SampleParams, w, z, y_saved, reg_accum, stream=None):
+    """Adds R = sum ||W (.) M~||^2 (Eq. 8) to reg_accum (float64, 1 element)."""
+    dev = w.device
+    f32 = _torch().float32
+    _check("maskgs_reg_reduce", load_library().maskgs_reg_reduce(
+        ctypes.byref(t.desc()), ctypes.byref(p),
+        _ptr(w, "w", numel=t.rows * t.cols, device=dev), _dtype_code(w),
+        _ptr(z, "z", f32, t.nblocks * t.k, dev),
+        _ptr(y_saved, "y_saved", f32, t.nblocks * t.k, dev),
+        _ptr(reg_accum, "reg_accum", _torch().float64, 1, dev), _stream(stream)))
+    return reg_accum
+
+
+def maskgs_hard_extract(t: Tensor, z, w=None, idx=None, mask_bits=None, values=None,
+                        val_idx=None, stream=None):
+    """argmax(z) per block, packed mask bits, 2:4 values and 2-bit indices."""
+    torch = _torch()
+    dev = z.device
+    B = t.nblocks
+    w_dt = _dtype_code(w) if w is not None else MASKGS_BF16
+    _check("maskgs_hard_extract", load_library().maskgs_hard_extract(
+        ctypes.byref(t.desc()), _ptr(z, "z", torch.float32, B * t.k, dev),
+        _ptr(w, "w", numel=t.rows * t.cols, device=dev), w_dt,
+        _ptr(idx, "idx", torch.uint8, B, dev),
+        _ptr(mask_bits, "mask_bits", torch.uint8, (B * t.m + 7) // 8, dev),
+        _ptr(values, "values", None if w is None else w.dtype, B * t.n, dev),
+        _ptr(val_idx, "val_idx", torch.uint8, (B + 1) // 2, dev), _stream(stream)))
+
+
+def maskgs_prior_init(t: Tensor, z, alpha: float, mode: int = 0, prior_bits=None, w=None,
+                      stream=None):
+    """Eq. 9-10 prior seeding of z in place (prior bits or magnitude top-N of w)."""
+    torch = _torch()
+    dev = z.device
+    B = t.nblocks
+    w_dt = _dtype_code(w) if w is not None else MASKGS_BF16
+    _check("maskgs_prior_init", load_library().maskgs_prior_init(
+        ctypes.byref(t.desc()), _ptr(z, "z", torch.float32, B * t.k, dev),
+        _ptr(prior_bits, "prior_bits", torch.uint8, (B * t.m + 7) // 8, dev),
+        _ptr(w, "w", numel=t.rows * t.cols, device=dev), w_dt, float(alpha), int(mode),
+        _stream(stream)))
+    return z
+
+
+def maskgs_debug_philox(seed: int, step: int, tensor_id: int, n0: int, words, stream=None):
+    torch = _torch()
+    _check("maskgs_debug_philox", load_library().maskgs_debug_philox(
+        seed, step, tensor_id, n0, words.numel(), _ptr(words, "words", torch.int32),
+        _stream(stream)))
+    return words
+
+
+def maskgs_debug_gumbel(words, g, stream=None):
+    torch = _torch()
+    _check("maskgs_debug_gumbel", load_library().maskgs_debug_gumbel(
+        _ptr(words, "words", torch.int32), words.numel(),
+        _ptr(g, "g", torch.float32, words.numel()), _stream(stream)))
+    return g

@@ -1,0 +1,625 @@
+// maskgs_k24.hip -- 2:4 kernels of libmaskgs for gfx950.
+//
+// Work item = one pair of consecutive blocks (2p, 2p+1) handled by one lane:
+//   weights   8 bf16 = one 16 B load (fp32: two),   logits 12 fp32 = three 16 B loads,
+//   and the pair's 12 noise words come from 3 Philox calls when the pair starts
+//   at an even global block (4 calls otherwise; PHASE is uniform per launch).
+// A workgroup walks tiles of 256 consecutive pairs (grid-stride, the same trip
+// count for every lane).  Inputs are read directly (lanes 48 B apart, three
+// 16 B loads each); 48-byte-per-lane outputs (soft index, logit gradient,
+// seeded logits) are transposed through LDS so that every global store is a
+// fully coalesced, non-temporal 16 B-per-lane stream.
+// The path is an HBM/VALU streaming path: no matrix cores are involved.
+#include <hip/hip_runtime.h>
+
+#include "maskgs_device.hpp"
+#include "maskgs_launch.hpp"
+
+namespace maskgs {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWavesPerCU = 8;  // grid cap: 8 workgroups of 256 per CU
+using C24 = Cands<2, 4>;
+
+// ---------------------------------------------------------------------------
+// Pair loads and stores.  `two` is false only for the last pair of an odd
+// block count; then only block 2p exists and only its bytes are touched.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void unpack_bf16x2(uint32_t v, float &lo, float &hi) {
+    lo = __uint_as_float(v << 16);
+    hi = __uint_as_float(v & 0xFFFF0000u);
+}
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct Io;
+
+template <>
+struct Io<bf16_t> {
+    static __device__ __forceinline__ void load8(const void *base, int64_t p, bool two,
+                                                 float (&v)[8]) {
+        const uint16_t *ptr = static_cast<const uint16_t *>(base) + p * 8;
+        if (two) {
+            const uint4 u = *reinterpret_cast<const uint4 *>(ptr);
+            unpack_bf16x2(u.x, v[0], v[1]);
+            unpack_bf16x2(u.y, v[2], v[3]);
+            unpack_bf16x2(u.z, v[4], v[5]);
+            unpack_bf16x2(u.w, v[6], v[7]);
+        } else {
+            const uint2 u = *reinterpret_cast<const uint2 *>(ptr);
+            unpack_bf16x2(u.x, v[0], v[1]);
+            unpack_bf16x2(u.y, v[2], v[3]);
+            v[4] = v[5] = v[6] = v[7] = 0.0f;
+        }
+    }
+    // raw bit patterns, widened to 32 bits
+    static __device__ __forceinline__ void load8_raw(const void *base, int64_t p, bool two,
+                                                     uint32_t (&r)[8]) {
+        const uint16_t *ptr = static_cast<const uint16_t *>(base) + p * 8;
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (two) {
+            u = *reinterpret_cast<const uint4 *>(ptr);
+        } else {
+            const uint2 h = *reinterpret_cast<const uint2 *>(ptr);
+            u.x = h.x;
+            u.y = h.y;
+        }
+        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            r[2 * i] = w4[i] & 0xFFFFu;
+            r[2 * i + 1] = w4[i] >> 16;
+        }
+    }
+    static __device__ __forceinline__ uint32_t magnitude(uint32_t raw) { return raw & 0x7FFFu; }
+    static __device__ __forceinline__ void store8(void *base, int64_t p, bool two,
+                                                  const float (&v)[8]) {
+        uint16_t *ptr = static_cast<uint16_t *>(base) + p * 8;
+        uint32_t u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            u[i] = static_cast<uint32_t>(bf16_rne(v[2 * i])) |
+                   (static_cast<uint32_t>(bf16_rne(v[2 * i + 1])) << 16);
+        if (two)
+            __builtin_nontemporal_store(v4u{u[0], u[1], u[2], u[3]}, reinterpret_cast<v4u *>(ptr));
+        else
+            *reinterpret_cast<uint2 *>(ptr) = make_uint2(u[0], u[1]);
+    }
+    // 2 kept values per block: 4 raw values for the pair (2 if only one block)
+    static __device__ __forceinline__ void store_values(void *base, int64_t p, bool two,
+                                                        const uint32_t (&r)[4]) {
+        uint16_t *ptr = static_cast<uint16_t *>(base) + p * 4;
+        const uint32_t a = r[0] | (r[1] << 16), b = r[2] | (r[3] << 16);
+        if (two)
+            *reinterpret_cast<uint2 *>(ptr) = make_uint2(a, b);
+        else
+            *reinterpret_cast<uint32_t *>(ptr) = a;
+    }
+};
+
+template <>
+struct Io<float> {
+    static __device__ __forceinline__ void load8(const void *base, int64_t p, bool two,
+                                                 float (&v)[8]) {
+        const float *ptr = static_cast<const float *>(base) + p * 8;
+        const float4 a = *reinterpret_cast<const float4 *>(ptr);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        if (two) {
+            const float4 b = *reinterpret_cast<const float4 *>(ptr + 4);
+            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        } else {
+            v[4] = v[5] = v[6] = v[7] = 0.0f;
+        }
+    }
+    static __device__ __forceinline__ void load8_raw(const void *base, int64_t p, bool two,
+                                                     uint32_t (&r)[8]) {
+        float v[8];
+        load8(base, p, two, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[i] = __float_as_uint(v[i]);
+    }
+    static __device__ __forceinline__ uint32_t magnitude(uint32_t raw) {
+        return raw & 0x7FFFFFFFu;
+    }
+    static __device__ __forceinline__ void store8(void *base, int64_t p, bool two,
+                                                  const float (&v)[8]) {
+        float *ptr = static_cast<float *>(base) + p * 8;
+        *reinterpret_cast<float4 *>(ptr) = make_float4(v[0], v[1], v[2], v[3]);
+        if (two) *reinterpret_cast<float4 *>(ptr + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    static __device__ __forceinline__ void store_values(void *base, int64_t p, bool two,
+                                                        const uint32_t (&r)[4]) {
+        uint32_t *ptr = static_cast<uint32_t *>(base) + p * 4;
+        if (two)
+            *reinterpret_cast<uint4 *>(ptr) = make_uint4(r[0], r[1], r[2], r[3]);
+        else
+            *reinterpret_cast<uint2 *>(ptr) = make_uint2(r[0], r[1]);
+    }
+};
+
+// 12 fp32 per pair ([2, 6] logits, soft indices or logit gradients)
+__device__ __forceinline__ void load12(const float *base, int64_t p, bool two, float (&v)[12]) {
+    const float *ptr = base + p * 12;
+    const float4 a = *reinterpret_cast<const float4 *>(ptr);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    if (two) {
+        const float4 b = *reinterpret_cast<const float4 *>(ptr + 4);
+        const float4 c = *reinterpret_cast<const float4 *>(ptr + 8);
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        v[8] = c.x; v[9] = c.y; v[10] = c.z; v[11] = c.w;
+    } else {
+        const float2 b = *reinterpret_cast<const float2 *>(ptr + 4);
+        v[4] = b.x; v[5] = b.y;
+        v[6] = v[7] = v[8] = v[9] = v[10] = v[11] = 0.0f;
+    }
+}
+
+__device__ __forceinline__ void nt_store(float4 *p, float4 v) {
+    __builtin_nontemporal_store(v4f{v.x, v.y, v.z, v.w}, reinterpret_cast<v4f *>(p));
+}
+
+// Stores 12 floats per lane for the workgroup tile of pairs [base, base+256):
+// lanes stage their values in LDS, then the tile (contiguous in memory) is
+// written with coalesced 16 B stores.  Called by every lane of the workgroup.
+__device__ __forceinline__ void store12_tile(float *g, int64_t base, int64_t nblocks,
+                                             const float (&v)[12], float4 *lds) {
+    const int t = threadIdx.x;
+    lds[3 * t] = make_float4(v[0], v[1], v[2], v[3]);
+    lds[3 * t + 1] = make_float4(v[4], v[5], v[6], v[7]);
+    lds[3 * t + 2] = make_float4(v[8], v[9], v[10], v[11]);
+    __syncthreads();
+    const int64_t end = 2 * (base + kThreads) < nblocks ? 2 * (base + kThreads) : nblocks;
+    const int nf = static_cast<int>((end - 2 * base) * 6);
+    const int n4 = nf >> 2;
+    float4 *dst = reinterpret_cast<float4 *>(g + base * 12);
+    for (int i = t; i < n4; i += kThreads) nt_store(dst + i, lds[i]);
+    if ((nf & 3) && t == 0)
+        reinterpret_cast<float2 *>(dst)[2 * n4] = reinterpret_cast<const float2 *>(lds)[2 * n4];
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Sampling (MaskLLM summary, section 3.4, Eqs. 5-7, Algorithm 1).
+// ---------------------------------------------------------------------------
+// Noise words of the pair starting at global block gb0 (PHASE = (6*gb0) % 4).
+template <int PHASE>
+__device__ __forceinline__ void pair_words(const Geometry &g, const Noise &nz, int64_t p,
+                                           uint32_t (&wd)[12]) {
+    const uint64_t gb0 = g.block_offset + 2 * static_cast<uint64_t>(p);
+    stream_words<12, PHASE>((gb0 * 6u) >> 2, nz.step, g.tensor_id, nz.k0, nz.k1, wd);
+}
+
+// Soft index of one block: a_i = fp32(fp32(kappa z_i + g_i) * fp32(1/tau)),
+// y = softmax(a) in fp32 (max-shifted, hardware exp2 and reciprocal).  The
+// exponentials are taken 2^64 too large, so that terms down to 2^-190 stay
+// normal through the exp2 (which flushes subnormal results); the product with
+// the reciprocal of the (equally scaled) sum then rounds small soft-index
+// values, subnormal ones included, correctly.
+__device__ __forceinline__ void soft_index6(const float *z, const uint32_t *wd, const Noise &nz,
+                                            float *y) {
+    float a[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+        const float g = nz.no_noise ? 0.0f : gumbel(wd[i]);
+        a[i] = __builtin_fmaf(nz.kappa, z[i], g) * nz.tau_inv;
+    }
+    float amax = a[0];
+#pragma unroll
+    for (int i = 1; i < 6; ++i) amax = fmaxf(amax, a[i]);
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+        a[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(a[i] - amax, 1.44269504088896341f, 64.0f));
+        s += a[i];
+    }
+    const float inv = __builtin_amdgcn_rcpf(s);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) y[i] = a[i] * inv;
+}
+
+// Soft mask m_j = sum_i y_i S_ij (Eq. 7), candidates in table order.
+__device__ __forceinline__ void soft_mask4(const float *y, float *m) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 6; ++i)
+            if ((C24::mask[i] >> j) & 1u) s += y[i];
+        m[j] = s;
+    }
+}
+
+template <int PHASE>
+__device__ __forceinline__ void pair_soft_index(const FwdArgs &a, int64_t p, const float (&z)[12],
+                                                float (&y)[12]) {
+    uint32_t wd[12];
+    if (!a.nz.no_noise) pair_words<PHASE>(a.g, a.nz, p, wd);
+    soft_index6(z, wd, a.nz, y);
+    soft_index6(z + 6, wd + 6, a.nz, y + 6);
+}
+
+// Workgroup sum of one double per lane, added atomically to *dst.
+__device__ __forceinline__ void reduce_add(double v, double *dst) {
+    __shared__ double part[kThreads / 64];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    if (lane == 0) part[wid] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double s = 0.0;
+#pragma unroll
+        for (int i = 0; i < kThreads / 64; ++i) s += part[i];
+        atomicAdd(dst, s);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Forward: W (.) M~, optional soft index and regulariser value.
+// ---------------------------------------------------------------------------
+template <int PHASE, typename WT, typename OT>
+__global__ __launch_bounds__(kThreads) void fwd24_kernel(FwdArgs a) {
+    __shared__ float4 stage[3 * kThreads];
+    const int64_t npairs = (a.g.nblocks + 1) >> 1;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    double reg = 0.0;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads; base < npairs;
+         base += stride) {
+        const int64_t p = base + threadIdx.x;
+        float y[12];
+        if (p < npairs) {
+            const bool two = 2 * p + 1 < a.g.nblocks;
+            float w[8], z[12], out[8];
+            Io<WT>::load8(a.w, p, two, w);
+            load12(a.z, p, two, z);
+            pair_soft_index<PHASE>(a, p, z, y);
+            float racc = 0.0f;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float m[4];
+                soft_mask4(y + 6 * h, m);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float u = w[4 * h + j] * m[j];
+                    out[4 * h + j] = u;
+                    racc = __builtin_fmaf(u, u, racc);
+                }
+            }
+            reg += static_cast<double>(racc);
+            Io<OT>::store8(a.out, p, two, out);
+        }
+        if (a.y) store12_tile(a.y, base, a.g.nblocks, y, stage);
+    }
+    if (a.reg) reduce_add(reg, a.reg);
+}
+
+// ---------------------------------------------------------------------------
+// Backward to the logits (section 3.2 information flow; section 3.4 Eq. 8):
+//   dm_j = G_j w_j - 2 lambda w_j (w_j m_j),  dy_i = sum_j S_ij dm_j,
+//   dz_i = (kappa/tau) y_i (dy_i - sum_k y_k dy_k)       (fp64 arithmetic)
+// ---------------------------------------------------------------------------
+template <int PHASE, typename WT, typename GT, bool SAVED>
+__global__ __launch_bounds__(kThreads) void bwd24_kernel(BwdArgs a) {
+    __shared__ float4 stage[3 * kThreads];
+    const int64_t npairs = (a.g.nblocks + 1) >> 1;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    const double two_lambda = 2.0 * a.lambda;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads; base < npairs;
+         base += stride) {
+        const int64_t p = base + threadIdx.x;
+        float dz[12];
+        if (p < npairs) {
+            const bool two = 2 * p + 1 < a.g.nblocks;
+            float w[8], G[8], y[12];
+            Io<WT>::load8(a.w, p, two, w);
+            Io<GT>::load8(a.dout, p, two, G);
+            if (SAVED) {
+                load12(a.y, p, two, y);
+            } else {
+                float z[12];
+                load12(a.z, p, two, z);
+                const FwdArgs f{a.w, a.z, nullptr, nullptr, nullptr, a.g, a.nz};
+                pair_soft_index<PHASE>(f, p, z, y);
+            }
+            float prev[12];
+            if (a.accumulate) load12(a.dz, p, two, prev);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float m[4];
+                soft_mask4(y + 6 * h, m);
+                double dm[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const double wj = static_cast<double>(w[4 * h + j]);
+                    const double u = wj * static_cast<double>(m[j]);
+                    dm[j] = static_cast<double>(G[4 * h + j]) * wj - two_lambda * wj * u;
+                }
+                double dy[6], s = 0.0;
+#pragma unroll
+                for (int i = 0; i < 6; ++i) {
+                    double t = 0.0;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if ((C24::mask[i] >> j) & 1u) t += dm[j];
+                    dy[i] = t;
+                    s += static_cast<double>(y[6 * h + i]) * t;
+                }
+#pragma unroll
+                for (int i = 0; i < 6; ++i) {
+                    double d = a.nz.grad_scale * static_cast<double>(y[6 * h + i]) * (dy[i] - s);
+                    if (a.accumulate) d += static_cast<double>(prev[6 * h + i]);
+                    dz[6 * h + i] = static_cast<float>(d);
+                }
+            }
+        }
+        store12_tile(a.dz, base, a.g.nblocks, dz, stage);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Regulariser value alone (section 3.4, Eq. 8).
+// ---------------------------------------------------------------------------
+template <int PHASE, typename WT, bool SAVED>
+__global__ __launch_bounds__(kThreads) void reg24_kernel(RegArgs a) {
+    const int64_t npairs = (a.g.nblocks + 1) >> 1;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    double reg = 0.0;
+    for (int64_t p = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; p < npairs;
+         p += stride) {
+        const bool two = 2 * p + 1 < a.g.nblocks;
+        float w[8], y[12];
+        Io<WT>::load8(a.w, p, two, w);
+        if (SAVED) {
+            load12(a.y, p, two, y);
+        } else {
+            float z[12];
+            load12(a.z, p, two, z);
+            const FwdArgs f{a.w, a.z, nullptr, nullptr, nullptr, a.g, a.nz};
+            pair_soft_index<PHASE>(f, p, z, y);
+        }
+        float racc = 0.0f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float m[4];
+            soft_mask4(y + 6 * h, m);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float u = w[4 * h + j] * m[j];
+                racc = __builtin_fmaf(u, u, racc);
+            }
+        }
+        reg += static_cast<double>(racc);
+    }
+    reduce_add(reg, a.reg);
+}
+
+// ---------------------------------------------------------------------------
+// Hard mask: argmax, packed bits, 2:4 values and 2-bit indices (section 3.2
+// inference flow; Algorithm 1 step 3).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int first_argmax6(const float *z) {
+    int best = 0;
+    float bv = z[0];
+#pragma unroll
+    for (int i = 1; i < 6; ++i)
+        if (z[i] > bv) {
+            bv = z[i];
+            best = i;
+        }
+    return best;
+}
+
+// The six candidate masks packed as nibbles (nibble i = mask i), so that a
+// runtime candidate index selects its mask with one shift.
+constexpr uint32_t pack_nibbles24() {
+    uint32_t v = 0;
+    for (int i = 0; i < 6; ++i) v |= static_cast<uint32_t>(C24::mask[i]) << (4 * i);
+    return v;
+}
+constexpr uint32_t kMaskNibbles24 = pack_nibbles24();
+
+__device__ __forceinline__ uint32_t cand_mask6(int k) { return (kMaskNibbles24 >> (4 * k)) & 0xFu; }
+
+__device__ __forceinline__ uint32_t pick4(const uint32_t *r, uint32_t pos) {
+    return pos == 0 ? r[0] : pos == 1 ? r[1] : pos == 2 ? r[2] : r[3];
+}
+
+template <typename WT>
+__global__ __launch_bounds__(kThreads) void hard24_kernel(HardArgs a) {
+    const int64_t npairs = (a.g.nblocks + 1) >> 1;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    for (int64_t p = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; p < npairs;
+         p += stride) {
+        const bool two = 2 * p + 1 < a.g.nblocks;
+        float z[12];
+        load12(a.z, p, two, z);
+        const int k0 = first_argmax6(z), k1 = first_argmax6(z + 6);
+        const uint32_t m0 = cand_mask6(k0), m1 = two ? cand_mask6(k1) : 0u;
+        if (a.idx) {
+            if (two)
+                *reinterpret_cast<uint16_t *>(a.idx + 2 * p) =
+                    static_cast<uint16_t>(k0 | (k1 << 8));
+            else
+                a.idx[2 * p] = static_cast<uint8_t>(k0);
+        }
+        if (a.bits) a.bits[p] = static_cast<uint8_t>(m0 | (m1 << 4));
+        const uint32_t lo0 = __builtin_ctz(m0), hi0 = 31 - __builtin_clz(m0);
+        const uint32_t lo1 = two ? __builtin_ctz(m1) : 0u, hi1 = two ? 31 - __builtin_clz(m1) : 0u;
+        if (a.val_idx)
+            a.val_idx[p] = static_cast<uint8_t>((lo0 | (hi0 << 2)) |
+                                                (two ? ((lo1 | (hi1 << 2)) << 4) : 0u));
+        if (a.values) {
+            uint32_t r[8];
+            Io<WT>::load8_raw(a.w, p, two, r);
+            const uint32_t v[4] = {pick4(r, lo0), pick4(r, hi0), pick4(r + 4, lo1),
+                                   pick4(r + 4, hi1)};
+            Io<WT>::store_values(a.values, p, two, v);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Prior seeding (section 3.4, Mask Prior, Eqs. 9-10).
+// ---------------------------------------------------------------------------
+// Magnitude top-2 of 4 magnitudes: position j is kept when fewer than 2
+// positions beat it (larger magnitude, or equal magnitude at a lower position).
+__device__ __forceinline__ uint32_t top2_of4(const uint32_t *mag) {
+    uint32_t keep = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        int beat = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (i != j) beat += (mag[i] > mag[j]) || (mag[i] == mag[j] && i < j);
+        if (beat < 2) keep |= 1u << j;
+    }
+    return keep;
+}
+
+__device__ __forceinline__ void prior_block6(float *z, uint32_t m0, double alpha, int mode) {
+    int dot[6], dsum = 0;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+        dot[i] = __builtin_popcount(m0 & C24::mask[i]);
+        dsum += dot[i];
+    }
+    if (mode == 0) {
+        const double mean = static_cast<double>(dsum) / 6.0;
+        double mu = 0.0;
+#pragma unroll
+        for (int i = 0; i < 6; ++i) mu += static_cast<double>(z[i]);
+        mu /= 6.0;
+        double var = 0.0;
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+            const double d = static_cast<double>(z[i]) - mu;
+            var += d * d;
+        }
+        const double sigma = sqrt(var / 6.0);
+#pragma unroll
+        for (int i = 0; i < 6; ++i)
+            z[i] = static_cast<float>(static_cast<double>(z[i]) +
+                                      alpha * sigma * (static_cast<double>(dot[i]) - mean));
+    } else {
+#pragma unroll
+        for (int i = 0; i < 6; ++i)
+            if (C24::mask[i] == m0) z[i] = static_cast<float>(static_cast<double>(z[i]) + alpha);
+    }
+}
+
+template <typename WT, bool BITS>
+__global__ __launch_bounds__(kThreads) void prior24_kernel(PriorArgs a) {
+    __shared__ float4 stage[3 * kThreads];
+    const int64_t npairs = (a.g.nblocks + 1) >> 1;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads; base < npairs;
+         base += stride) {
+        const int64_t p = base + threadIdx.x;
+        float z[12];
+        if (p < npairs) {
+            const bool two = 2 * p + 1 < a.g.nblocks;
+            load12(a.z, p, two, z);
+            uint32_t m0, m1;
+            if (BITS) {
+                const uint32_t byte = a.prior_bits[p];
+                m0 = byte & 0xFu;
+                m1 = byte >> 4;
+            } else {
+                uint32_t r[8], mag[8];
+                Io<WT>::load8_raw(a.w, p, two, r);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) mag[j] = Io<WT>::magnitude(r[j]);
+                m0 = top2_of4(mag);
+                m1 = top2_of4(mag + 4);
+            }
+            prior_block6(z, m0, a.alpha, a.mode);
+            prior_block6(z + 6, m1, a.alpha, a.mode);
+        }
+        // in place: store12_tile's barrier orders every lane's loads before the stores
+        store12_tile(a.z, base, a.g.nblocks, z, stage);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launch helpers.
+// ---------------------------------------------------------------------------
+template <typename K, typename A>
+hipError_t go(K kernel, const A &args, int64_t items, hipStream_t s) {
+    const unsigned grid = grid_for(items, kThreads, kWavesPerCU);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, s, args);
+    return hipGetLastError();
+}
+
+int phase_of(uint64_t block_offset) { return (block_offset & 1u) ? 2 : 0; }
+
+template <int PHASE>
+hipError_t fwd24_dispatch(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype o_dt,
+                          hipStream_t s) {
+    const int64_t np = (a.g.nblocks + 1) >> 1;
+    if (w_dt == MASKGS_BF16 && o_dt == MASKGS_BF16)
+        return go(fwd24_kernel<PHASE, bf16_t, bf16_t>, a, np, s);
+    if (w_dt == MASKGS_BF16 && o_dt == MASKGS_F32)
+        return go(fwd24_kernel<PHASE, bf16_t, float>, a, np, s);
+    if (w_dt == MASKGS_F32 && o_dt == MASKGS_BF16)
+        return go(fwd24_kernel<PHASE, float, bf16_t>, a, np, s);
+    return go(fwd24_kernel<PHASE, float, float>, a, np, s);
+}
+
+template <int PHASE, bool SAVED>
+hipError_t bwd24_dispatch(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt,
+                          hipStream_t s) {
+    const int64_t np = (a.g.nblocks + 1) >> 1;
+    if (w_dt == MASKGS_BF16 && g_dt == MASKGS_BF16)
+        return go(bwd24_kernel<PHASE, bf16_t, bf16_t, SAVED>, a, np, s);
+    if (w_dt == MASKGS_BF16 && g_dt == MASKGS_F32)
+        return go(bwd24_kernel<PHASE, bf16_t, float, SAVED>, a, np, s);
+    if (w_dt == MASKGS_F32 && g_dt == MASKGS_BF16)
+        return go(bwd24_kernel<PHASE, float, bf16_t, SAVED>, a, np, s);
+    return go(bwd24_kernel<PHASE, float, float, SAVED>, a, np, s);
+}
+
+template <int PHASE, bool SAVED>
+hipError_t reg24_dispatch(const RegArgs &a, maskgs_dtype w_dt, hipStream_t s) {
+    const int64_t np = (a.g.nblocks + 1) >> 1;
+    if (w_dt == MASKGS_BF16) return go(reg24_kernel<PHASE, bf16_t, SAVED>, a, np, s);
+    return go(reg24_kernel<PHASE, float, SAVED>, a, np, s);
+}
+
+}  // namespace
+
+hipError_t launch_fwd24(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype out_dt, hipStream_t s) {
+    return phase_of(a.g.block_offset) == 0 ? fwd24_dispatch<0>(a, w_dt, out_dt, s)
+                                           : fwd24_dispatch<2>(a, w_dt, out_dt, s);
+}
+
+hipError_t launch_bwd24(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, hipStream_t s) {
+    const bool even = phase_of(a.g.block_offset) == 0;
+    if (a.y) return even ? bwd24_dispatch<0, true>(a, w_dt, g_dt, s)
+                         : bwd24_dispatch<2, true>(a, w_dt, g_dt, s);
+    return even ? bwd24_dispatch<0, false>(a, w_dt, g_dt, s)
+                : bwd24_dispatch<2, false>(a, w_dt, g_dt, s);
+}
+
+hipError_t launch_reg24(const RegArgs &a, maskgs_dtype w_dt, hipStream_t s) {
+    const bool even = phase_of(a.g.block_offset) == 0;
+    if (a.y) return even ? reg24_dispatch<0, true>(a, w_dt, s) : reg24_dispatch<2, true>(a, w_dt, s);
+    return even ? reg24_dispatch<0, false>(a, w_dt, s) : reg24_dispatch<2, false>(a, w_dt, s);
+}
+
+hipError_t launch_hard24(const HardArgs &a, maskgs_dtype w_dt, hipStream_t s) {
+    const int64_t np = (a.g.nblocks + 1) >> 1;
+    if (a.values && w_dt == MASKGS_F32) return go(hard24_kernel<float>, a, np, s);
+    return go(hard24_kernel<bf16_t>, a, np, s);
+}
+
+hipError_t launch_prior24(const PriorArgs &a, maskgs_dtype w_dt, hipStream_t s) {
+    const int64_t np = (a.g.nblocks + 1) >> 1;
+    if (a.prior_bits) return go(prior24_kernel<bf16_t, true>, a, np, s);
+    if (w_dt == MASKGS_F32) return go(prior24_kernel<float, false>, a, np, s);
+    return go(prior24_kernel<bf16_t, false>, a, np, s);
+}
+
+}  // namespace maskgs

@@ -1,0 +1,612 @@
+// maskgs_k48.hip -- 4:8 kernels of libmaskgs for gfx950.
+//
+// Work item = one block per lane (70 candidates, K = C(8,4)); a workgroup is
+// one wave and walks tiles of 64 consecutive blocks.  Logit-sized streams
+// (280 B per block) always cross HBM as fully coalesced 16 B-per-lane copies
+// through LDS.  Two kernel shapes:
+//  - noise kernels (forward; backward and regulariser that recompute the soft
+//    index) are VALU-bound: the 70 values of a block live in registers and the
+//    LDS stage holds 32 blocks (8960 B) at a time;
+//  - the other kernels (backward and regulariser from a saved soft index, hard
+//    mask, prior) are HBM-bound: the whole 64-block tile (17920 B) stays in
+//    LDS and each lane reads and rewrites its own 70-value row there, which
+//    keeps register use low.
+// Weights, upstream gradients and masked weights (8 elements per block) are
+// loaded and stored directly.
+// The candidate table (70 masks, lexicographic) is a compile-time constant:
+// every use below is unrolled, so it folds into the instruction stream.
+//
+// Noise: block gb uses stream words 70*gb .. 70*gb+69, i.e. Philox calls
+// q0 .. q0+17 (q0 = 70*gb/4) starting at word 0 (gb even) or word 2 (gb odd).
+// Lanes of a wave alternate between the two phases, so each chunk of four
+// candidates takes its words from the current call or from the current and
+// the next call by a per-lane select; register indices stay static.
+#include <hip/hip_runtime.h>
+
+#include "maskgs_device.hpp"
+#include "maskgs_launch.hpp"
+
+namespace maskgs {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kK = 70;
+constexpr int kHalf = 32;  // blocks staged per LDS round
+constexpr int kWgPerCU = 16;
+using C48 = Cands<4, 8>;
+
+// ---------------------------------------------------------------------------
+// Tile transfers through LDS.  Tile = blocks [b0, b0+nb), b0 a multiple of 64,
+// so every half tile starts 16-byte aligned (280 B * even block index).
+// All lanes of the wave call these (they contain barriers).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int half_count(int nb, int h) {
+    const int c = nb - h * kHalf;
+    return c < 0 ? 0 : (c > kHalf ? kHalf : c);
+}
+
+template <bool ADD>
+__device__ __forceinline__ void tile_in(const float *g, int64_t b0, int nb, float *stage,
+                                        float (&v)[kK]) {
+    const int lane = threadIdx.x;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int cnt = half_count(nb, h);
+        const float *src = g + (b0 + h * kHalf) * kK;
+        const int nf = cnt * kK, n4 = nf >> 2;
+        for (int i = lane; i < n4; i += kWave)
+            reinterpret_cast<float4 *>(stage)[i] = reinterpret_cast<const float4 *>(src)[i];
+        if ((nf & 3) && lane == 0)
+            reinterpret_cast<float2 *>(stage)[2 * n4] = reinterpret_cast<const float2 *>(src)[2 * n4];
+        __syncthreads();
+        const int j = lane - h * kHalf;
+        if (j >= 0 && j < cnt) {
+            const float2 *row = reinterpret_cast<const float2 *>(stage) + j * (kK / 2);
+#pragma unroll
+            for (int t = 0; t < kK / 2; ++t) {
+                const float2 u = row[t];
+                if (ADD) {
+                    v[2 * t] = static_cast<float>(static_cast<double>(v[2 * t]) + u.x);
+                    v[2 * t + 1] = static_cast<float>(static_cast<double>(v[2 * t + 1]) + u.y);
+                } else {
+                    v[2 * t] = u.x;
+                    v[2 * t + 1] = u.y;
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+__device__ __forceinline__ void tile_out(float *g, int64_t b0, int nb, float *stage,
+                                         const float (&v)[kK]) {
+    const int lane = threadIdx.x;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int cnt = half_count(nb, h);
+        const int j = lane - h * kHalf;
+        if (j >= 0 && j < cnt) {
+            float2 *row = reinterpret_cast<float2 *>(stage) + j * (kK / 2);
+#pragma unroll
+            for (int t = 0; t < kK / 2; ++t) row[t] = make_float2(v[2 * t], v[2 * t + 1]);
+        }
+        __syncthreads();
+        float *dst = g + (b0 + h * kHalf) * kK;
+        const int nf = cnt * kK, n4 = nf >> 2;
+        for (int i = lane; i < n4; i += kWave)
+            reinterpret_cast<float4 *>(dst)[i] = reinterpret_cast<const float4 *>(stage)[i];
+        if ((nf & 3) && lane == 0)
+            reinterpret_cast<float2 *>(dst)[2 * n4] = reinterpret_cast<const float2 *>(stage)[2 * n4];
+        __syncthreads();
+    }
+}
+
+// Whole-tile copies (64 blocks = 17920 B, 16-byte aligned): global <-> LDS.
+__device__ __forceinline__ void tile_copy_in(const float *g, int64_t b0, int nb, float *lds) {
+    const int lane = threadIdx.x;
+    const float *src = g + b0 * kK;
+    const int nf = nb * kK, n4 = nf >> 2;
+    for (int i = lane; i < n4; i += kWave)
+        reinterpret_cast<float4 *>(lds)[i] = reinterpret_cast<const float4 *>(src)[i];
+    if ((nf & 3) && lane == 0)
+        reinterpret_cast<float2 *>(lds)[2 * n4] = reinterpret_cast<const float2 *>(src)[2 * n4];
+}
+
+__device__ __forceinline__ void tile_copy_out(float *g, int64_t b0, int nb, const float *lds) {
+    const int lane = threadIdx.x;
+    float *dst = g + b0 * kK;
+    const int nf = nb * kK, n4 = nf >> 2;
+    for (int i = lane; i < n4; i += kWave)
+        reinterpret_cast<float4 *>(dst)[i] = reinterpret_cast<const float4 *>(lds)[i];
+    if ((nf & 3) && lane == 0)
+        reinterpret_cast<float2 *>(dst)[2 * n4] = reinterpret_cast<const float2 *>(lds)[2 * n4];
+}
+
+// 8 weights / gradients of one block.
+template <typename T>
+struct Io8;
+
+template <>
+struct Io8<bf16_t> {
+    static __device__ __forceinline__ void load(const void *base, int64_t b, float (&v)[8]) {
+        const uint4 u = reinterpret_cast<const uint4 *>(base)[b];
+        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w4[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w4[i] & 0xFFFF0000u);
+        }
+    }
+    static __device__ __forceinline__ void load_mag(const void *base, int64_t b, uint32_t (&m)[8]) {
+        const uint4 u = reinterpret_cast<const uint4 *>(base)[b];
+        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            m[2 * i] = w4[i] & 0x7FFFu;
+            m[2 * i + 1] = (w4[i] >> 16) & 0x7FFFu;
+        }
+    }
+    static __device__ __forceinline__ void store(void *base, int64_t b, const float (&v)[8]) {
+        uint32_t u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            u[i] = static_cast<uint32_t>(bf16_rne(v[2 * i])) |
+                   (static_cast<uint32_t>(bf16_rne(v[2 * i + 1])) << 16);
+        reinterpret_cast<uint4 *>(base)[b] = make_uint4(u[0], u[1], u[2], u[3]);
+    }
+};
+
+template <>
+struct Io8<float> {
+    static __device__ __forceinline__ void load(const void *base, int64_t b, float (&v)[8]) {
+        const float4 a = reinterpret_cast<const float4 *>(base)[2 * b];
+        const float4 c = reinterpret_cast<const float4 *>(base)[2 * b + 1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+    }
+    static __device__ __forceinline__ void load_mag(const void *base, int64_t b, uint32_t (&m)[8]) {
+        float v[8];
+        load(base, b, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m[i] = __float_as_uint(v[i]) & 0x7FFFFFFFu;
+    }
+    static __device__ __forceinline__ void store(void *base, int64_t b, const float (&v)[8]) {
+        reinterpret_cast<float4 *>(base)[2 * b] = make_float4(v[0], v[1], v[2], v[3]);
+        reinterpret_cast<float4 *>(base)[2 * b + 1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Sampling (MaskLLM summary, section 3.4, Eqs. 5-7, Algorithm 1).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void philox_call(uint64_t q, uint32_t step, uint32_t tid, uint32_t k0,
+                                            uint32_t k1, uint32_t (&x)[4]) {
+    x[0] = static_cast<uint32_t>(q);
+    x[1] = static_cast<uint32_t>(q >> 32);
+    x[2] = step;
+    x[3] = tid;
+    philox10(x[0], x[1], x[2], x[3], k0, k1);
+}
+
+// v: logits z on entry, a_i = fp32(fp32(kappa z_i + g_i) * fp32(1/tau)) on exit.
+__device__ __forceinline__ void logits70(float (&v)[kK], uint64_t gb, const Geometry &g,
+                                         const Noise &nz) {
+    if (nz.no_noise) {
+#pragma unroll
+        for (int i = 0; i < kK; ++i) v[i] = __builtin_fmaf(nz.kappa, v[i], 0.0f) * nz.tau_inv;
+        return;
+    }
+    const uint64_t n0 = gb * static_cast<uint64_t>(kK);
+    const uint64_t q0 = n0 >> 2;
+    const bool odd = (n0 & 3u) != 0;
+    uint32_t prev[4];
+    philox_call(q0, nz.step, g.tensor_id, nz.k0, nz.k1, prev);
+#pragma unroll
+    for (int c = 0; c < 18; ++c) {
+        uint32_t cur[4] = {0u, 0u, 0u, 0u};
+        if (c < 17) philox_call(q0 + static_cast<uint64_t>(c + 1), nz.step, g.tensor_id, nz.k0,
+                                nz.k1, cur);
+        const uint32_t wd[4] = {odd ? prev[2] : prev[0], odd ? prev[3] : prev[1],
+                                odd ? cur[0] : prev[2], odd ? cur[1] : prev[3]};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = 4 * c + u;
+            if (i < kK) v[i] = __builtin_fmaf(nz.kappa, v[i], gumbel(wd[u])) * nz.tau_inv;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) prev[u] = cur[u];
+    }
+}
+
+// In place: a -> y = softmax(a) (Eq. 6).  Exponentials scaled by 2^64 so that
+// small soft-index values are rounded correctly instead of flushed.
+__device__ __forceinline__ void softmax70(float (&v)[kK]) {
+    float amax = v[0];
+#pragma unroll
+    for (int i = 1; i < kK; ++i) amax = fmaxf(amax, v[i]);
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kK; ++i) {
+        v[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i] - amax, 1.44269504088896341f, 64.0f));
+        s += v[i];
+    }
+    const float inv = __builtin_amdgcn_rcpf(s);
+#pragma unroll
+    for (int i = 0; i < kK; ++i) v[i] *= inv;
+}
+
+// Soft mask m_j = sum_i y_i S_ij (Eq. 7), candidates in table order.
+__device__ __forceinline__ void soft_mask8(const float (&y)[kK], float (&m)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kK; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if ((C48::at(i) >> j) & 1u) m[j] += y[i];
+}
+
+__device__ __forceinline__ void reduce_add_wave(double v, double *dst) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if (threadIdx.x == 0) atomicAdd(dst, v);
+}
+
+__device__ __forceinline__ int64_t tile_count(int64_t nblocks) {
+    return (nblocks + kWave - 1) / kWave;
+}
+
+// ---------------------------------------------------------------------------
+// Forward (noise kernel, registers).
+// ---------------------------------------------------------------------------
+template <typename WT, typename OT>
+__global__ __launch_bounds__(kWave) void fwd48_kernel(FwdArgs a) {
+    __shared__ float4 stage4[kHalf * kK / 4];
+    float *stage = reinterpret_cast<float *>(stage4);
+    const int lane = threadIdx.x;
+    const int64_t ntiles = tile_count(a.g.nblocks);
+    double reg = 0.0;
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t b0 = tile * kWave;
+        const int nb = static_cast<int>(a.g.nblocks - b0 < kWave ? a.g.nblocks - b0 : kWave);
+        const int64_t b = b0 + lane;
+        float v[kK];
+        tile_in<false>(a.z, b0, nb, stage, v);
+        if (lane < nb) {
+            logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz);
+            softmax70(v);
+            float m[8], w[8], out[8];
+            soft_mask8(v, m);
+            Io8<WT>::load(a.w, b, w);
+            float racc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                out[j] = w[j] * m[j];
+                racc = __builtin_fmaf(out[j], out[j], racc);
+            }
+            reg += static_cast<double>(racc);
+            Io8<OT>::store(a.out, b, out);
+        }
+        if (a.y) tile_out(a.y, b0, nb, stage, v);
+    }
+    if (a.reg) reduce_add_wave(reg, a.reg);
+}
+
+// ---------------------------------------------------------------------------
+// Regulariser value (section 3.4, Eq. 8), recomputing the soft index.
+// ---------------------------------------------------------------------------
+template <typename WT>
+__global__ __launch_bounds__(kWave) void reg48_noise_kernel(RegArgs a) {
+    __shared__ float4 stage4[kHalf * kK / 4];
+    float *stage = reinterpret_cast<float *>(stage4);
+    const int lane = threadIdx.x;
+    const int64_t ntiles = tile_count(a.g.nblocks);
+    double reg = 0.0;
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t b0 = tile * kWave;
+        const int nb = static_cast<int>(a.g.nblocks - b0 < kWave ? a.g.nblocks - b0 : kWave);
+        const int64_t b = b0 + lane;
+        float v[kK];
+        tile_in<false>(a.z, b0, nb, stage, v);
+        if (lane < nb) {
+            logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz);
+            softmax70(v);
+            float m[8], w[8];
+            soft_mask8(v, m);
+            Io8<WT>::load(a.w, b, w);
+            float racc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float u = w[j] * m[j];
+                racc = __builtin_fmaf(u, u, racc);
+            }
+            reg += static_cast<double>(racc);
+        }
+    }
+    reduce_add_wave(reg, a.reg);
+}
+
+// ---------------------------------------------------------------------------
+// LDS-resident kernels: one 64-block tile in LDS, lane = row of 70 values.
+// ---------------------------------------------------------------------------
+// Compiler barrier between passes over an LDS row: the row is re-read from LDS
+// in each pass instead of being kept in registers across passes.
+__device__ __forceinline__ void row_pass_barrier() { asm volatile("" ::: "memory"); }
+
+// Soft mask of a row in fp32 and fp64 (Eq. 7).
+__device__ __forceinline__ void row_soft_mask(const float *row, float (&m)[8], double (&md)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        m[j] = 0.0f;
+        md[j] = 0.0;
+    }
+#pragma unroll
+    for (int i = 0; i < kK; ++i) {
+        const float y = row[i];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if ((C48::at(i) >> j) & 1u) {
+                m[j] += y;
+                md[j] += static_cast<double>(y);
+            }
+    }
+}
+
+// Backward (section 3.2 information flow; section 3.4 Eq. 8), fp64 arithmetic:
+// dm_j = G_j w_j - 2 lambda w_j (w_j m_j); sum_i y_i dy_i = sum_j m_j dm_j;
+// dz_i = (kappa/tau) y_i (dy_i - sum_j m_j dm_j), dy_i = sum_{j in S_i} dm_j.
+template <typename WT, typename GT, bool SAVED, bool ACC>
+__global__ __launch_bounds__(kWave) void bwd48_kernel(BwdArgs a) {
+    __shared__ float4 tile4[kWave * kK / 4];
+    __shared__ float4 prev4[ACC ? kWave * kK / 4 : 1];
+    float *tl = reinterpret_cast<float *>(tile4);
+    const float *pv = reinterpret_cast<const float *>(prev4);
+    const int lane = threadIdx.x;
+    const int64_t ntiles = tile_count(a.g.nblocks);
+    const double two_lambda = 2.0 * a.lambda;
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t b0 = tile * kWave;
+        const int nb = static_cast<int>(a.g.nblocks - b0 < kWave ? a.g.nblocks - b0 : kWave);
+        const int64_t b = b0 + lane;
+        tile_copy_in(SAVED ? a.y : a.z, b0, nb, tl);
+        if (ACC) tile_copy_in(a.dz, b0, nb, reinterpret_cast<float *>(prev4));
+        __syncthreads();
+        float *row = tl + lane * kK;
+        if (lane < nb) {
+            if (!SAVED) {
+                float v[kK];
+#pragma unroll
+                for (int i = 0; i < kK; ++i) v[i] = row[i];
+                logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz);
+                softmax70(v);
+#pragma unroll
+                for (int i = 0; i < kK; ++i) row[i] = v[i];
+                row_pass_barrier();
+            }
+            float m[8], w[8], G[8];
+            double md[8], dm[8];
+            row_soft_mask(row, m, md);
+            Io8<WT>::load(a.w, b, w);
+            Io8<GT>::load(a.dout, b, G);
+            double s = 0.0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const double wj = static_cast<double>(w[j]);
+                dm[j] = static_cast<double>(G[j]) * wj - two_lambda * wj * (wj * m[j]);
+                s += md[j] * dm[j];
+            }
+            row_pass_barrier();
+            const float *prow = pv + lane * kK;
+#pragma unroll
+            for (int i = 0; i < kK; ++i) {
+                double dy = 0.0;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if ((C48::at(i) >> j) & 1u) dy += dm[j];
+                double d = a.nz.grad_scale * static_cast<double>(row[i]) * (dy - s);
+                if (ACC) d += static_cast<double>(prow[i]);
+                row[i] = static_cast<float>(d);
+            }
+        }
+        __syncthreads();
+        tile_copy_out(a.dz, b0, nb, tl);
+        __syncthreads();
+    }
+}
+
+// Regulariser value from a saved soft index.
+template <typename WT>
+__global__ __launch_bounds__(kWave) void reg48_saved_kernel(RegArgs a) {
+    __shared__ float4 tile4[kWave * kK / 4];
+    const float *tl = reinterpret_cast<const float *>(tile4);
+    const int lane = threadIdx.x;
+    const int64_t ntiles = tile_count(a.g.nblocks);
+    double reg = 0.0;
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t b0 = tile * kWave;
+        const int nb = static_cast<int>(a.g.nblocks - b0 < kWave ? a.g.nblocks - b0 : kWave);
+        tile_copy_in(a.y, b0, nb, reinterpret_cast<float *>(tile4));
+        __syncthreads();
+        if (lane < nb) {
+            float m[8], w[8];
+            double md[8];
+            row_soft_mask(tl + lane * kK, m, md);
+            Io8<WT>::load(a.w, b0 + lane, w);
+            float racc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float u = w[j] * m[j];
+                racc = __builtin_fmaf(u, u, racc);
+            }
+            reg += static_cast<double>(racc);
+        }
+        __syncthreads();
+    }
+    reduce_add_wave(reg, a.reg);
+}
+
+// Hard mask: argmax index and packed bits (one byte per 4:8 block).
+__global__ __launch_bounds__(kWave) void hard48_kernel(HardArgs a) {
+    __shared__ float4 tile4[kWave * kK / 4];
+    const float *tl = reinterpret_cast<const float *>(tile4);
+    const int lane = threadIdx.x;
+    const int64_t ntiles = tile_count(a.g.nblocks);
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t b0 = tile * kWave;
+        const int nb = static_cast<int>(a.g.nblocks - b0 < kWave ? a.g.nblocks - b0 : kWave);
+        tile_copy_in(a.z, b0, nb, reinterpret_cast<float *>(tile4));
+        __syncthreads();
+        if (lane < nb) {
+            const float *row = tl + lane * kK;
+            int best = 0;
+            float bv = row[0];
+#pragma unroll
+            for (int i = 1; i < kK; ++i) {
+                const float x = row[i];
+                if (x > bv) {
+                    bv = x;
+                    best = i;
+                }
+            }
+            if (a.idx) a.idx[b0 + lane] = static_cast<uint8_t>(best);
+            if (a.bits) {
+                uint32_t mask = C48::at(0);
+#pragma unroll
+                for (int i = 1; i < kK; ++i)
+                    if (best == i) mask = C48::at(i);
+                a.bits[b0 + lane] = static_cast<uint8_t>(mask);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Prior seeding (section 3.4, Mask Prior, Eqs. 9-10).
+__device__ __forceinline__ uint32_t top4_of8(const uint32_t (&mag)[8]) {
+    uint32_t keep = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        int beat = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i != j) beat += (mag[i] > mag[j]) || (mag[i] == mag[j] && i < j);
+        if (beat < 4) keep |= 1u << j;
+    }
+    return keep;
+}
+
+template <typename WT, bool BITS>
+__global__ __launch_bounds__(kWave) void prior48_kernel(PriorArgs a) {
+    __shared__ float4 tile4[kWave * kK / 4];
+    float *tl = reinterpret_cast<float *>(tile4);
+    const int lane = threadIdx.x;
+    const int64_t ntiles = tile_count(a.g.nblocks);
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t b0 = tile * kWave;
+        const int nb = static_cast<int>(a.g.nblocks - b0 < kWave ? a.g.nblocks - b0 : kWave);
+        const int64_t b = b0 + lane;
+        tile_copy_in(a.z, b0, nb, tl);
+        __syncthreads();
+        if (lane < nb) {
+            float *row = tl + lane * kK;
+            uint32_t m0;
+            if (BITS) {
+                m0 = a.prior_bits[b];
+            } else {
+                uint32_t mag[8];
+                Io8<WT>::load_mag(a.w, b, mag);
+                m0 = top4_of8(mag);
+            }
+            if (a.mode == 0) {
+                int dsum = 0;
+#pragma unroll
+                for (int i = 0; i < kK; ++i) dsum += __builtin_popcount(m0 & C48::at(i));
+                const double mean = static_cast<double>(dsum) / static_cast<double>(kK);
+                double mu = 0.0;
+#pragma unroll
+                for (int i = 0; i < kK; ++i) mu += static_cast<double>(row[i]);
+                mu /= static_cast<double>(kK);
+                row_pass_barrier();
+                double var = 0.0;
+#pragma unroll
+                for (int i = 0; i < kK; ++i) {
+                    const double d = static_cast<double>(row[i]) - mu;
+                    var += d * d;
+                }
+                const double scale = a.alpha * sqrt(var / static_cast<double>(kK));
+                row_pass_barrier();
+#pragma unroll
+                for (int i = 0; i < kK; ++i) {
+                    const double sim =
+                        static_cast<double>(__builtin_popcount(m0 & C48::at(i))) - mean;
+                    row[i] = static_cast<float>(static_cast<double>(row[i]) + scale * sim);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < kK; ++i)
+                    if (C48::at(i) == m0)
+                        row[i] = static_cast<float>(static_cast<double>(row[i]) + a.alpha);
+            }
+        }
+        __syncthreads();
+        tile_copy_out(a.z, b0, nb, tl);
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launch helpers.
+// ---------------------------------------------------------------------------
+template <typename Kern, typename A>
+hipError_t go(Kern kernel, const A &args, int64_t nblocks, hipStream_t s) {
+    const unsigned grid = grid_for((nblocks + kWave - 1) / kWave, 1, kWgPerCU);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kWave), 0, s, args);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd48(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype out_dt, hipStream_t s) {
+    const int64_t n = a.g.nblocks;
+    if (w_dt == MASKGS_BF16 && out_dt == MASKGS_BF16) return go(fwd48_kernel<bf16_t, bf16_t>, a, n, s);
+    if (w_dt == MASKGS_BF16) return go(fwd48_kernel<bf16_t, float>, a, n, s);
+    if (out_dt == MASKGS_BF16) return go(fwd48_kernel<float, bf16_t>, a, n, s);
+    return go(fwd48_kernel<float, float>, a, n, s);
+}
+
+template <bool SAVED, bool ACC>
+hipError_t bwd48_dispatch(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, hipStream_t s) {
+    const int64_t n = a.g.nblocks;
+    const bool wb = w_dt == MASKGS_BF16, gb = g_dt == MASKGS_BF16;
+    if (wb && gb) return go(bwd48_kernel<bf16_t, bf16_t, SAVED, ACC>, a, n, s);
+    if (wb) return go(bwd48_kernel<bf16_t, float, SAVED, ACC>, a, n, s);
+    if (gb) return go(bwd48_kernel<float, bf16_t, SAVED, ACC>, a, n, s);
+    return go(bwd48_kernel<float, float, SAVED, ACC>, a, n, s);
+}
+
+hipError_t launch_bwd48(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, hipStream_t s) {
+    if (a.y) return a.accumulate ? bwd48_dispatch<true, true>(a, w_dt, g_dt, s)
+                                 : bwd48_dispatch<true, false>(a, w_dt, g_dt, s);
+    return a.accumulate ? bwd48_dispatch<false, true>(a, w_dt, g_dt, s)
+                        : bwd48_dispatch<false, false>(a, w_dt, g_dt, s);
+}
+
+hipError_t launch_reg48(const RegArgs &a, maskgs_dtype w_dt, hipStream_t s) {
+    const int64_t n = a.g.nblocks;
+    if (w_dt == MASKGS_BF16)
+        return a.y ? go(reg48_saved_kernel<bf16_t>, a, n, s) : go(reg48_noise_kernel<bf16_t>, a, n, s);
+    return a.y ? go(reg48_saved_kernel<float>, a, n, s) : go(reg48_noise_kernel<float>, a, n, s);
+}
+
+hipError_t launch_hard48(const HardArgs &a, hipStream_t s) {
+    return go(hard48_kernel, a, a.g.nblocks, s);
+}
+
+hipError_t launch_prior48(const PriorArgs &a, maskgs_dtype w_dt, hipStream_t s) {
+    const int64_t n = a.g.nblocks;
+    if (a.prior_bits) return go(prior48_kernel<bf16_t, true>, a, n, s);
+    if (w_dt == MASKGS_F32) return go(prior48_kernel<float, false>, a, n, s);
+    return go(prior48_kernel<bf16_t, false>, a, n, s);
+}
+
+}  // namespace maskgs

@@ -1,0 +1,105 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point that include/maskgs.h declares, and rejects bad arguments
+with the documented status before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import REPO
+
+import sparsity_masks_weights_amd as mg
+
+HEADER = os.path.join(REPO, "include", "maskgs.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    return mg.load_library()
+
+
+def test_exports_every_declared_symbol(L):
+    decl = set(re.findall(r"\b(maskgs_\w+)\s*\(", open(HEADER).read()))
+    assert decl == set(mg.EXPORTS)
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+def test_abi_version_and_status_strings(L):
+    assert mg.maskgs_abi_version() == 1
+    for s in range(0, 10):
+        assert isinstance(L.maskgs_status_str(s), bytes)
+
+
+def test_candidates_match_oracle_tables(orc):
+    assert mg.maskgs_candidates(2, 4) == orc.candidates(2, 4).tolist()
+    assert mg.maskgs_candidates(4, 8) == orc.candidates(4, 8).tolist()
+    with pytest.raises(mg.MaskgsError) as e:
+        mg.maskgs_candidates(1, 4)
+    assert e.value.status == mg.MASKGS_E_UNSUPPORTED
+    buf = (ctypes.c_uint8 * 8)()
+    assert mg.load_library().maskgs_candidates(4, 8, buf, 8, None) == mg.MASKGS_E_CAPACITY
+
+
+A = 1 << 20  # a 16-byte aligned fake device address: never dereferenced
+
+
+def _fwd(L, desc=None, params=None, w=A, w_dt=1, z=A, out=A, out_dt=1, y=None, reg=None):
+    d = desc or mg.TensorDesc(2, 4, 8, 16, 0, 0)
+    p = params or mg.SampleParams(0, 0, 100.0, 4.0, 0)
+    return L.maskgs_fwd(ctypes.byref(d), ctypes.byref(p), w, w_dt, z, out, out_dt, y, reg, None)
+
+
+def test_fwd_validation(L):
+    assert _fwd(L, desc=mg.TensorDesc(3, 8, 8, 16, 0, 0)) == mg.MASKGS_E_UNSUPPORTED
+    assert _fwd(L, desc=mg.TensorDesc(2, 4, 8, 18, 0, 0)) == mg.MASKGS_E_SHAPE
+    assert _fwd(L, desc=mg.TensorDesc(2, 4, -1, 16, 0, 0)) == mg.MASKGS_E_SHAPE
+    assert _fwd(L, params=mg.SampleParams(0, 0, 100.0, 0.0, 0)) == mg.MASKGS_E_RANGE
+    assert _fwd(L, params=mg.SampleParams(0, 0, -1.0, 1.0, 0)) == mg.MASKGS_E_RANGE
+    assert _fwd(L, params=mg.SampleParams(0, 0, float("nan"), 1.0, 0)) == mg.MASKGS_E_RANGE
+    assert _fwd(L, params=mg.SampleParams(0, 0, 1.0, float("inf"), 0)) == mg.MASKGS_E_RANGE
+    assert _fwd(L, params=mg.SampleParams(0, 0, 1.0, 1e-45, 0)) == mg.MASKGS_E_RANGE
+    assert _fwd(L, w=None) == mg.MASKGS_E_NULL
+    assert _fwd(L, z=None) == mg.MASKGS_E_NULL
+    assert _fwd(L, out=None) == mg.MASKGS_E_NULL
+    assert _fwd(L, w_dt=7) == mg.MASKGS_E_DTYPE
+    assert _fwd(L, out=A + 8) == mg.MASKGS_E_ALIGN
+    assert _fwd(L, y=A + 4) == mg.MASKGS_E_ALIGN
+    assert L.maskgs_fwd(None, None, A, 1, A, A, 1, None, None, None) == mg.MASKGS_E_NULL
+    # empty tensors launch nothing and succeed
+    assert _fwd(L, desc=mg.TensorDesc(2, 4, 0, 16, 0, 0)) == mg.MASKGS_OK
+    assert _fwd(L, desc=mg.TensorDesc(4, 8, 5, 0, 0, 0)) == mg.MASKGS_OK
+    assert _fwd(L, desc=mg.TensorDesc(2, 4, 0, 16, 0, 0), w=None, z=None, out=None) == mg.MASKGS_OK
+
+
+def test_bwd_reg_hard_prior_validation(L):
+    d = mg.TensorDesc(2, 4, 8, 16, 0, 0)
+    p = mg.SampleParams(0, 0, 100.0, 4.0, 0)
+    bd, bp = ctypes.byref(d), ctypes.byref(p)
+    assert L.maskgs_bwd(bd, bp, A, 1, None, None, A, 1, 1e-5, A, 0, None) == mg.MASKGS_E_NULL
+    assert L.maskgs_bwd(bd, bp, A, 1, A, None, A, 1, -1.0, A, 0, None) == mg.MASKGS_E_RANGE
+    assert L.maskgs_bwd(bd, bp, A, 1, A, None, A, 3, 1e-5, A, 0, None) == mg.MASKGS_E_DTYPE
+    assert L.maskgs_bwd(bd, bp, A, 1, A, None, A + 2, 1, 1e-5, A, 0, None) == mg.MASKGS_E_ALIGN
+    assert L.maskgs_reg_reduce(bd, bp, A, 1, A, None, None, None) == mg.MASKGS_E_NULL
+    assert L.maskgs_hard_extract(bd, None, None, 1, A, None, None, None, None) == mg.MASKGS_E_NULL
+    assert L.maskgs_hard_extract(bd, A, None, 1, None, None, A, None, None) == mg.MASKGS_E_NULL
+    d48 = mg.TensorDesc(4, 8, 8, 16, 0, 0)
+    assert L.maskgs_hard_extract(ctypes.byref(d48), A, A, 1, None, None, A, None,
+                                 None) == mg.MASKGS_E_UNSUPPORTED
+    assert L.maskgs_hard_extract(ctypes.byref(d48), A, None, 1, None, None, None, A,
+                                 None) == mg.MASKGS_E_UNSUPPORTED
+    assert L.maskgs_prior_init(bd, A, None, None, 1, 3.0, 0, None) == mg.MASKGS_E_NULL
+    assert L.maskgs_prior_init(bd, A, A, None, 1, -1.0, 0, None) == mg.MASKGS_E_RANGE
+    assert L.maskgs_prior_init(bd, A, A, None, 1, 3.0, 2, None) == mg.MASKGS_E_RANGE
+    assert L.maskgs_prior_init(bd, A + 1, A, None, 1, 3.0, 0, None) == mg.MASKGS_E_ALIGN
+    assert L.maskgs_debug_philox(0, 0, 0, 0, -1, A, None) == mg.MASKGS_E_SHAPE
+    assert L.maskgs_debug_gumbel(A, 4, None, None) == mg.MASKGS_E_NULL
+
+
+def test_python_wrapper_refuses_cpu_tensors():
+    import torch
+    t = mg.Tensor(2, 4, 4, 8)
+    w = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mg.maskgs_fwd(t, mg.sample_params(), w, torch.zeros(8, 6), torch.zeros_like(w))
