@@ -1,0 +1,278 @@
+"""Benchmark of the differentiable N:M mask path on one MI355X.
+
+One step = one pass of the hot path over every linear weight of a 32-layer
+LLaMA-2-7B-shaped model (224 tensors, 1.62e9 2:4 blocks, inputs resident in
+HBM): the Gumbel soft-mask forward of every tensor (W (.) M~ in bf16, soft
+index saved, regulariser reduced), then the logit backward of every tensor
+(from the saved soft index), then hard-mask extraction with bit packing and
+2:4 compaction of every tensor.  Prior seeding, an initialisation step, is
+timed once after the steps and reported beside them.
+
+Prints ONE JSON line.  `value` = 2:4 weight blocks per second through the whole
+step; `roofline` describes the kernel with the largest share of the step;
+`cpu_baseline` times the CPU oracle (all host threads) on a bounded sample of
+the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+REPO = os.path.dirname(os.path.abspath(__file__))
+if REPO not in sys.path:
+    sys.path.insert(0, REPO)
+
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(REPO, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = ["sparsity_masks_weights_amd/csrc/maskgs_k24.hip",
+                  "sparsity_masks_weights_amd/csrc/maskgs_device.hpp"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama7b_all_linear")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="use only the first L layers (profiling runs; default: all)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(REPO, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the mask path shards by rows with no "
+              "exchange, and this build measures one GPU's share (use --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparsity_masks_weights_amd as mg
+    from workloads import WORKLOADS, tensor_inputs
+
+    L = mg.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    wl = WORKLOADS[args.workload]
+    specs = wl.tensors
+    if args.layers is not None:
+        specs = [t for t in specs if t.tensor_id < 7 * args.layers]
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    # ---- resident inputs and outputs --------------------------------------
+    bufs = []
+    for spec in specs:
+        w, z, G = tensor_inputs(wl, spec, dev)
+        B = spec.rows * spec.cols // wl.m
+        d = dict(spec=spec, w=w, z=z, G=G,
+                 out=torch.empty_like(w), y=torch.empty_like(z), dz=torch.empty_like(z),
+                 bits=torch.empty((B * wl.m + 7) // 8, dtype=torch.uint8, device=dev),
+                 vals=torch.empty(B * wl.n, dtype=w.dtype, device=dev),
+                 vidx=torch.empty((B + 1) // 2, dtype=torch.uint8, device=dev))
+        d["desc"] = mg.TensorDesc(wl.n, wl.m, spec.rows, spec.cols, 0, spec.tensor_id)
+        d["B"] = B
+        bufs.append(d)
+    reg = torch.zeros(1, dtype=torch.float64, device=dev)
+    total_blocks = sum(d["B"] for d in bufs)
+    torch.cuda.synchronize()
+
+    bf = mg.MASKGS_BF16
+    P = ctypes.c_void_p
+
+    def ptr(t):
+        return P(t.data_ptr())
+
+    # pre-marshalled argument tuples: the timed loop only calls the C ABI
+    calls = {"fwd": [], "bwd": [], "hard": []}
+    params = [mg.SampleParams(0, 0, wl.kappa, wl.tau, 0)]
+    pref = ctypes.byref(params[0])
+    for d in bufs:
+        dref = ctypes.byref(d["desc"])
+        calls["fwd"].append((L.maskgs_fwd, (dref, pref, ptr(d["w"]), bf, ptr(d["z"]), ptr(d["out"]),
+                                            bf, ptr(d["y"]), ptr(reg), sptr)))
+        calls["bwd"].append((L.maskgs_bwd, (dref, pref, ptr(d["w"]), bf, None, ptr(d["y"]),
+                                            ptr(d["G"]), bf, ctypes.c_float(wl.lam), ptr(d["dz"]), 0,
+                                            sptr)))
+        calls["hard"].append((L.maskgs_hard_extract, (dref, ptr(d["z"]), ptr(d["w"]), bf, None,
+                                                       ptr(d["bits"]), ptr(d["vals"]),
+                                                       ptr(d["vidx"]), sptr)))
+
+    ev = {k: [] for k in calls}
+
+    def step(record: bool):
+        reg.zero_()
+        for kind in ("fwd", "bwd", "hard"):
+            for fn, a in calls[kind]:
+                if record:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                rc = fn(*a)
+                if rc != 0:
+                    raise RuntimeError(f"{kind}: status {rc}")
+                if record:
+                    e1.record(stream)
+                    ev[kind].append((e0, e1))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for s in range(args.steps):
+        params[0].step = s
+        step(True)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+
+    # ---- per-kernel statistics (HIP events on the launch stream) ----------
+    per_block_bytes = {"fwd": 8 + 24 + 8 + 24, "bwd": 8 + 24 + 8 + 24,
+                       "hard": 24 + 8 + 0.5 + 4 + 0.5}
+    kstats = {}
+    for kind, pairs in ev.items():
+        times = [a.elapsed_time(b) for a, b in pairs]
+        tot = sum(times) / args.steps
+        # the largest tensor class dominates; report an average over all launches
+        nl = len(pairs) // args.steps
+        avg_us = 1e3 * sum(times) / len(times)
+        bytes_per_step = per_block_bytes[kind] * total_blocks
+        kstats[kind] = dict(ms_per_step=round(tot, 4), launches_per_step=nl,
+                            avg_launch_us=round(avg_us, 2),
+                            algorithmic_bytes_per_block=per_block_bytes[kind],
+                            achieved_gbs=round(bytes_per_step / (tot * 1e-3) / 1e9, 1))
+    dom = max(kstats, key=lambda k: kstats[k]["ms_per_step"])
+
+    # roofline of the dominant kernel: one launch on the largest tensors
+    # (11008x4096, 11.27M blocks) -- the launch shape profiled by rocprofv3
+    big = [i for i, d in enumerate(bufs) if d["B"] == max(x["B"] for x in bufs)]
+    nl = len(bufs)
+    big_times = [ev[dom][s * nl + i][0].elapsed_time(ev[dom][s * nl + i][1])
+                 for s in range(args.steps) for i in big]
+    big_ms = sum(big_times) / len(big_times)
+    big_bytes = per_block_bytes[dom] * bufs[big[0]]["B"]
+    achieved = big_bytes / (big_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        k = tr.get("kernels", {}).get(dom)
+        if k and tr.get("source_hash") == source_hash():
+            traffic = k.get("hbm_bytes_per_launch")
+    roofline = dict(bound="hbm", kernel=f"maskgs_{dom} (2:4, 11008x4096 bf16 tensor)",
+                    achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
+                    avg_launch_us=round(big_ms * 1e3, 2),
+                    algorithmic_bytes_per_launch=int(big_bytes))
+
+    # ---- prior seeding, timed once (initialisation row of the path) -------
+    pe0 = torch.cuda.Event(enable_timing=True)
+    pe1 = torch.cuda.Event(enable_timing=True)
+    pe0.record(stream)
+    for d in bufs:
+        rc = L.maskgs_prior_init(ctypes.byref(d["desc"]), ptr(d["z"]), None, ptr(d["w"]), bf,
+                                 ctypes.c_float(3.0), 0, sptr)
+        if rc != 0:
+            raise RuntimeError(f"prior_init: status {rc}")
+    pe1.record(stream)
+    torch.cuda.synchronize()
+    prior_ms = pe0.elapsed_time(pe1)
+
+    if args.calibrate_copy:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    fwd_bwd_ms = kstats["fwd"]["ms_per_step"] + kstats["bwd"]["ms_per_step"]
+    result = {
+        "metric": "weight-blocks/s and HBM GB/s (% of peak), 2:4 mask fwd+bwd, LLaMA-2-7B shapes",
+        "value": round(total_blocks / (ms_step * 1e-3), 1),
+        "unit": "weight-blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.key, "tensors": len(bufs), "blocks": total_blocks,
+                   "n_m": f"{wl.n}:{wl.m}", "weights": "bf16 N(0,0.02)",
+                   "logits": "fp32 N(0,1)", "upstream_grad": "bf16 N(0,1e-3)",
+                   "kappa": wl.kappa, "tau": wl.tau, "lambda": wl.lam,
+                   "step": "fwd (y saved, reg) + bwd (saved y) + hard extract/pack/compact",
+                   "parallelism": "single GPU"},
+        "fwd_bwd_blocks_per_s": round(total_blocks / (fwd_bwd_ms * 1e-3), 1),
+        "fwd_bwd_hbm_gbs": round(128 * total_blocks / (fwd_bwd_ms * 1e-3) / 1e9, 1),
+        "kernels": kstats,
+        "prior_init": {"ms_all_tensors": round(prior_ms, 3),
+                       "achieved_gbs": round(56 * total_blocks / (prior_ms * 1e-3) / 1e9, 1)},
+        "roofline": roofline,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, bufs, mg)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, bufs, mg):
+    """The CPU oracle (all host threads) on layer 0: fwd + bwd + hard extract."""
+    import numpy as np
+    import torch
+    import oracle
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count() or 1
+    oracle.set_threads(threads)
+    used = oracle.get_threads()
+    sample = [d for d in bufs if d["spec"].tensor_id < 7]
+    blocks = 0
+    secs = 0.0
+    for d in sample:
+        spec = d["spec"]
+        wu = d["w"].view(torch.int16).cpu().numpy().view(np.uint16)
+        wf = oracle.widen_bf16(wu).reshape(spec.rows, spec.cols)
+        zf = d["z"].cpu().numpy()
+        gf = oracle.widen_bf16(d["G"].view(torch.int16).cpu().numpy().view(np.uint16))
+        gf = gf.reshape(spec.rows, spec.cols)
+        kw = dict(kappa=wl.kappa, tau=wl.tau, seed=0, step=0, tensor_id=spec.tensor_id)
+        t = time.perf_counter()
+        oracle.fwd(wl.n, wl.m, wf, zf, **kw)
+        oracle.bwd(wl.n, wl.m, wf, zf, gf, lam=wl.lam, **kw)
+        oracle.hard_extract(wl.n, wl.m, zf, spec.rows, spec.cols, w_raw=wu)
+        secs += time.perf_counter() - t
+        blocks += d["B"]
+        del wu, wf, zf, gf
+    return {"value": round(blocks / secs, 1), "unit": "weight-blocks/s", "cores": used,
+            "kind": "oracle",
+            "sample": f"layer 0 of the same workload ({len(sample)} tensors, {blocks} blocks): "
+                      f"fwd + bwd + hard extract, {secs:.1f} s of CPU time"}
+
+
+if __name__ == "__main__":
+    main()

@@ -192,32 +192,26 @@ __device__ __forceinline__ void pair_words(const Geometry &g, const Noise &nz, i
     stream_words<12, PHASE>((gb0 * 6u) >> 2, nz.step, g.tensor_id, nz.k0, nz.k1, wd);
 }
 
-// Soft index of one block: a_i = fp32(fp32(kappa z_i + g_i) * fp32(1/tau)),
-// y = softmax(a) in fp32 (max-shifted, hardware exp2 and reciprocal).  The
-// exponentials are taken 2^64 too large, so that terms down to 2^-190 stay
-// normal through the exp2 (which flushes subnormal results); the product with
-// the reciprocal of the (equally scaled) sum then rounds small soft-index
-// values, subnormal ones included, correctly.
-__device__ __forceinline__ void soft_index6(const float *z, const uint32_t *wd, const Noise &nz,
-                                            float *y) {
-    float a[6];
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-        const float g = nz.no_noise ? 0.0f : gumbel(wd[i]);
-        a[i] = __builtin_fmaf(nz.kappa, z[i], g) * nz.tau_inv;
-    }
+// Soft index of one block from its perturbed logits: y = softmax(a) in fp32
+// (max-shifted, hardware exp2 and reciprocal).  The exponentials are taken
+// 2^64 too large, so that terms down to 2^-190 stay normal through the exp2
+// (which flushes subnormal results); the product with the reciprocal of the
+// (equally scaled) sum then rounds small soft-index values, subnormal ones
+// included, correctly.
+__device__ __forceinline__ void softmax6(const float *a, float *y) {
+    float e[6];
     float amax = a[0];
 #pragma unroll
     for (int i = 1; i < 6; ++i) amax = fmaxf(amax, a[i]);
     float s = 0.0f;
 #pragma unroll
     for (int i = 0; i < 6; ++i) {
-        a[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(a[i] - amax, 1.44269504088896341f, 64.0f));
-        s += a[i];
+        e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(a[i] - amax, 1.44269504088896341f, 64.0f));
+        s += e[i];
     }
     const float inv = __builtin_amdgcn_rcpf(s);
 #pragma unroll
-    for (int i = 0; i < 6; ++i) y[i] = a[i] * inv;
+    for (int i = 0; i < 6; ++i) y[i] = e[i] * inv;
 }
 
 // Soft mask m_j = sum_i y_i S_ij (Eq. 7), candidates in table order.
@@ -232,13 +226,26 @@ __device__ __forceinline__ void soft_mask4(const float *y, float *m) {
     }
 }
 
+// Soft index of a pair (section 3.4, Eq. 6 and Algorithm 1 steps 1-2):
+// a_i = fp32(fp32(kappa z_i + g_i) * fp32(1/tau)) with g the contract noise.
+// The noise flag is uniform, so the twelve Gumbel evaluations form one
+// straight-line block the scheduler can interleave.
 template <int PHASE>
 __device__ __forceinline__ void pair_soft_index(const FwdArgs &a, int64_t p, const float (&z)[12],
                                                 float (&y)[12]) {
-    uint32_t wd[12];
-    if (!a.nz.no_noise) pair_words<PHASE>(a.g, a.nz, p, wd);
-    soft_index6(z, wd, a.nz, y);
-    soft_index6(z + 6, wd + 6, a.nz, y + 6);
+    float a12[12];
+    if (a.nz.no_noise) {
+#pragma unroll
+        for (int i = 0; i < 12; ++i) a12[i] = __builtin_fmaf(a.nz.kappa, z[i], 0.0f) * a.nz.tau_inv;
+    } else {
+        uint32_t wd[12];
+        pair_words<PHASE>(a.g, a.nz, p, wd);
+#pragma unroll
+        for (int i = 0; i < 12; ++i)
+            a12[i] = __builtin_fmaf(a.nz.kappa, z[i], -neg_gumbel(wd[i])) * a.nz.tau_inv;
+    }
+    softmax6(a12, y);
+    softmax6(a12 + 6, y + 6);
 }
 
 // Workgroup sum of one double per lane, added atomically to *dst.
@@ -337,7 +344,10 @@ __global__ __launch_bounds__(kThreads) void bwd24_kernel(BwdArgs a) {
                     const double u = wj * static_cast<double>(m[j]);
                     dm[j] = static_cast<double>(G[4 * h + j]) * wj - two_lambda * wj * u;
                 }
-                double dy[6], s = 0.0;
+                // s = sum_k y_k dy_k / sum_k y_k: dividing by the actual sum of
+                // the fp32 soft index keeps dy_i - s free of the fp32 rounding
+                // of y (for the dominant candidate it is a sum over the others)
+                double dy[6], s = 0.0, ysum = 0.0;
 #pragma unroll
                 for (int i = 0; i < 6; ++i) {
                     double t = 0.0;
@@ -346,7 +356,9 @@ __global__ __launch_bounds__(kThreads) void bwd24_kernel(BwdArgs a) {
                         if ((C24::mask[i] >> j) & 1u) t += dm[j];
                     dy[i] = t;
                     s += static_cast<double>(y[6 * h + i]) * t;
+                    ysum += static_cast<double>(y[6 * h + i]);
                 }
+                s /= ysum;
 #pragma unroll
                 for (int i = 0; i < 6; ++i) {
                     double d = a.nz.grad_scale * static_cast<double>(y[6 * h + i]) * (dy[i] - s);

@@ -354,7 +354,8 @@ __device__ __forceinline__ void row_soft_mask(const float *row, float (&m)[8], d
 
 // Backward (section 3.2 information flow; section 3.4 Eq. 8), fp64 arithmetic:
 // dm_j = G_j w_j - 2 lambda w_j (w_j m_j); sum_i y_i dy_i = sum_j m_j dm_j;
-// dz_i = (kappa/tau) y_i (dy_i - sum_j m_j dm_j), dy_i = sum_{j in S_i} dm_j.
+// dz_i = (kappa/tau) y_i (dy_i - s), dy_i = sum_{j in S_i} dm_j, with
+// s = sum_i y_i dy_i / sum_i y_i.
 template <typename WT, typename GT, bool SAVED, bool ACC>
 __global__ __launch_bounds__(kWave) void bwd48_kernel(BwdArgs a) {
     __shared__ float4 tile4[kWave * kK / 4];
@@ -388,13 +389,18 @@ __global__ __launch_bounds__(kWave) void bwd48_kernel(BwdArgs a) {
             row_soft_mask(row, m, md);
             Io8<WT>::load(a.w, b, w);
             Io8<GT>::load(a.dout, b, G);
-            double s = 0.0;
+            // s = sum_i y_i dy_i / sum_i y_i = sum_j m_j dm_j / (sum_j m_j / 4): the
+            // division by the actual sum of the fp32 soft index keeps dy_i - s
+            // free of the fp32 rounding of y (see the 2:4 backward)
+            double s = 0.0, msum = 0.0;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const double wj = static_cast<double>(w[j]);
                 dm[j] = static_cast<double>(G[j]) * wj - two_lambda * wj * (wj * m[j]);
                 s += md[j] * dm[j];
+                msum += md[j];
             }
+            s = s * 4.0 / msum;
             row_pass_barrier();
             const float *prow = pv + lane * kK;
 #pragma unroll

@@ -125,6 +125,7 @@ CASES = [
     (37, 36, "bf16", 0, 5, 9, 3, 100.0, 4.0, 1.0),       # odd block count: ragged pair
     (37, 36, "bf16", 7, 5, 9, 3, 100.0, 4.0, 1.0),       # odd global offset: 4-call pairs
     (64, 1024, "bf16", 123456789, 11, 2**40 + 3, 5, 500.0, 0.05, 1.0),   # annealed end
+    (64, 1024, "f32", 5, 12, 7, 5, 500.0, 0.05, 1.0),    # annealed end, large dL/dM
     (300, 512, "bf16", 2, 224, 1, 9, 250.0, 1.0, 0.01),  # small logits, many workgroups
     (1, 4, "f32", 0, 0, 0, 0, 100.0, 4.0, 1.0),          # a single block
     (3, 8, "f32", 1, 0, 0, 0, 100.0, 4.0, 1.0),

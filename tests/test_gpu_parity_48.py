@@ -1,0 +1,171 @@
+"""GPU parity of the 4:8 path (70 candidates per block) against the CPU oracle.
+
+Small shapes in full (several 64-block tiles and a ragged last tile, odd and
+even global block offsets so that both Philox word phases occur in every
+wave), then the Nemotron-4-15B-shaped layer set at full size on sampled rows.
+Bars as for 2:4: noise and integer outputs bit-exact, soft index / logit
+gradient / prior logits / regulariser within 1e-6 + 1e-5|ref|, bf16 masked
+weights within one bf16 ulp.
+"""
+import numpy as np
+import pytest
+
+from conftest import gpu_available
+from gpu_helpers import assert_bf16_ulp, assert_close, assert_out, to_np, widen
+from test_gpu_workloads import check_rows, run_tensor
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+K = 70
+
+
+@pytest.fixture(scope="module")
+def mg():
+    import sparsity_masks_weights_amd as mg
+    mg.load_library()
+    return mg
+
+
+def _rand(shape, std, dtype, seed):
+    import torch
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    return (torch.randn(shape, generator=g, device=dev) * std).to(dtype)
+
+
+CASES = [
+    # rows, cols, w dtype, block_offset, tensor_id, seed, step, kappa, tau
+    (16, 128, "bf16", 0, 0, 0, 0, 100.0, 2.0),
+    (37, 72, "bf16", 3, 4, 11, 2, 100.0, 2.0),     # 333 blocks: ragged tile
+    (5, 8, "f32", 1, 1, 2, 0, 100.0, 2.0),        # 5 blocks
+    (64, 512, "f32", 12345, 9, 2**33 + 1, 7, 500.0, 0.05),
+    (130, 64, "bf16", 2, 3, 5, 1, 10.0, 8.0),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_small_shapes_full(mg, orc, case):
+    import torch
+    rows, cols, wdt, off, tid, seed, step, kappa, tau = case
+    dt = torch.float32 if wdt == "f32" else torch.bfloat16
+    B = rows * cols // 8
+    w = _rand((rows, cols), 0.015, dt, 30 + tid)
+    z = _rand((B, K), 1.0, torch.float32, 31 + tid)
+    G = _rand((rows, cols), 1e-3 if wdt == "bf16" else 1.0, dt, 32 + tid)
+    t = mg.Tensor(4, 8, rows, cols, off, tid)
+    p = mg.sample_params(seed, step, kappa, tau)
+    dev = w.device
+    out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+    y = torch.empty_like(z)
+    reg = torch.zeros(1, dtype=torch.float64, device=dev)
+    mg.maskgs_fwd(t, p, w, z, out, y, reg)
+    dz_r = torch.empty_like(z)
+    mg.maskgs_bwd(t, p, w, z, None, G, 1e-5, dz_r)
+    dz_s = torch.empty_like(z)
+    mg.maskgs_bwd(t, p, w, None, y, G, 1e-5, dz_s)
+    idx = torch.empty(B, dtype=torch.uint8, device=dev)
+    bits = torch.empty(B, dtype=torch.uint8, device=dev)
+    mg.maskgs_hard_extract(t, z, None, idx, bits)
+    r2 = torch.zeros_like(reg)
+    r3 = torch.zeros_like(reg)
+    mg.maskgs_reg_reduce(t, p, w, z, None, r2)
+    mg.maskgs_reg_reduce(t, p, w, None, y, r3)
+    torch.cuda.synchronize()
+
+    wf, zn, Gf = widen(to_np(w)), to_np(z), widen(to_np(G))
+    kw = dict(kappa=kappa, tau=tau, seed=seed, step=step, tensor_id=tid, block_offset=off)
+    f = orc.fwd(4, 8, wf, zn, **kw)
+    d = orc.bwd(4, 8, wf, zn, Gf, lam=1e-5, **kw)
+    h = orc.hard_extract(4, 8, zn, rows, cols)
+    what = str(case)
+    assert_close(to_np(y), f["y"], f"{what} y")
+    assert_bf16_ulp(to_np(out), f["out"], f"{what} out")
+    for r in (reg, r2, r3):
+        assert abs(r.item() - f["reg"]) <= 1e-5 * f["reg"], (what, r.item(), f["reg"])
+    assert_close(to_np(dz_r), d, f"{what} dz recompute")
+    assert_close(to_np(dz_s), d, f"{what} dz saved")
+    assert np.array_equal(to_np(dz_r), to_np(dz_s)), what
+    assert np.array_equal(to_np(idx), h["idx"]), what
+    assert np.array_equal(to_np(bits), h["bits"]), what
+
+
+def test_fp32_out_no_noise_and_accumulate(mg, orc):
+    import torch
+    rows, cols = 9, 64
+    B = rows * cols // 8
+    w = _rand((rows, cols), 0.015, torch.bfloat16, 40)
+    z = _rand((B, K), 1.0, torch.float32, 41)
+    G = _rand((rows, cols), 1e-3, torch.float32, 42)
+    t = mg.Tensor(4, 8, rows, cols, 7, 2)
+    p = mg.sample_params(3, 1, 100.0, 2.0, mg.MASKGS_NO_NOISE)
+    out = torch.empty((rows, cols), dtype=torch.float32, device=w.device)
+    y = torch.empty_like(z)
+    mg.maskgs_fwd(t, p, w, z, out, y)
+    kw = dict(kappa=100.0, tau=2.0, seed=3, step=1, tensor_id=2, block_offset=7,
+              flags=orc.NO_NOISE)
+    f = orc.fwd(4, 8, widen(to_np(w)), to_np(z), out_dtype="f32", **kw)
+    assert_close(to_np(y), f["y"], "no-noise y")
+    assert_out(to_np(out), f["out"], "fp32 out")
+    p = mg.sample_params(3, 1, 100.0, 2.0)
+    kw.pop("flags")
+    prev = _rand((B, K), 1e-3, torch.float32, 43)
+    for saved in (False, True):
+        dz = prev.clone()
+        if saved:
+            mg.maskgs_fwd(t, p, w, z, out, y)
+            mg.maskgs_bwd(t, p, w, None, y, G, 0.3, dz, accumulate=True)
+        else:
+            mg.maskgs_bwd(t, p, w, z, None, G, 0.3, dz, accumulate=True)
+        ref = orc.bwd(4, 8, widen(to_np(w)), to_np(z), to_np(G), lam=0.3, dz_prev=to_np(prev),
+                      **kw)
+        assert_close(to_np(dz), ref, f"accumulate saved={saved}")
+
+
+@pytest.mark.parametrize("mode,source", [(0, "bits"), (1, "bits"), (0, "w_bf16"), (1, "w_f32")])
+def test_prior_init_48(mg, orc, mode, source):
+    import torch
+    rows, cols = 21, 64
+    B = rows * cols // 8
+    wdt = torch.float32 if source == "w_f32" else torch.bfloat16
+    w = _rand((rows, cols), 0.015, wdt, 44)
+    w[0, :8] = 0.25  # ties keep the lower positions
+    z = _rand((B, K), 0.01, torch.float32, 45)
+    zz = z.clone()
+    t = mg.Tensor(4, 8, rows, cols)
+    if source == "bits":
+        rng = np.random.default_rng(9)
+        cand = np.array(orc.candidates(4, 8), dtype=np.uint8)
+        bits_np = cand[rng.integers(0, 70, size=B)]
+        bits_np[::13] = 0b00011111  # five kept positions: matches no candidate
+        mg.maskgs_prior_init(t, zz, 3.0, mode, prior_bits=torch.from_numpy(bits_np).cuda())
+        ref = orc.prior_init(4, 8, to_np(z), rows, cols, alpha=3.0, mode=mode,
+                             prior_bits=bits_np)
+    else:
+        mg.maskgs_prior_init(t, zz, 3.0, mode, w=w)
+        ref = orc.prior_init(4, 8, to_np(z), rows, cols, alpha=3.0, mode=mode,
+                             w=widen(to_np(w)))
+    assert_close(to_np(zz), ref, f"4:8 prior mode {mode} {source}")
+
+
+def test_nemotron_layer_sampled_rows(mg, orc):
+    """Nemotron-4-15B-shaped layer set at 4:8: fwd + bwd on sampled rows,
+    argmax indices and packed masks in full."""
+    import torch
+    from workloads import WORKLOADS, tensor_inputs
+    wl = WORKLOADS["nemotron15b_layer_48"]
+    dev = torch.device("cuda:0")
+    for spec in wl.tensors:
+        w, z, G = tensor_inputs(wl, spec, dev)
+        p = mg.sample_params(0, 0, wl.kappa, wl.tau)
+        t, out, y, dz, reg = run_tensor(mg, wl, spec, dev, p, w, z, G)
+        check_rows(orc, 4, 8, spec, p, w, z, G, wl.lam, y, out, dz, spec.name)
+        bits = torch.empty(t.nblocks, dtype=torch.uint8, device=dev)
+        idx = torch.empty(t.nblocks, dtype=torch.uint8, device=dev)
+        mg.maskgs_hard_extract(t, z, None, idx, bits)
+        h = orc.hard_extract(4, 8, to_np(z), spec.rows, spec.cols)
+        assert np.array_equal(to_np(idx), h["idx"]), spec.name
+        assert np.array_equal(to_np(bits), h["bits"]), spec.name
+        del w, z, G, out, y, dz
+        torch.cuda.empty_cache()
