@@ -30,6 +30,7 @@ if REPO not in sys.path:
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(REPO, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = ["sparsity_masks_weights_amd/csrc/maskgs_k24.hip",
+                  "sparsity_masks_weights_amd/csrc/maskgs_k48.hip",
                   "sparsity_masks_weights_amd/csrc/maskgs_device.hpp"]
 
 
@@ -82,14 +83,15 @@ def main():
 
     # ---- resident inputs and outputs --------------------------------------
     bufs = []
+    compact = (wl.n, wl.m) == (2, 4)  # values + 2-bit indices exist for 2:4 only
     for spec in specs:
         w, z, G = tensor_inputs(wl, spec, dev)
         B = spec.rows * spec.cols // wl.m
         d = dict(spec=spec, w=w, z=z, G=G,
                  out=torch.empty_like(w), y=torch.empty_like(z), dz=torch.empty_like(z),
                  bits=torch.empty((B * wl.m + 7) // 8, dtype=torch.uint8, device=dev),
-                 vals=torch.empty(B * wl.n, dtype=w.dtype, device=dev),
-                 vidx=torch.empty((B + 1) // 2, dtype=torch.uint8, device=dev))
+                 vals=torch.empty(B * wl.n, dtype=w.dtype, device=dev) if compact else None,
+                 vidx=torch.empty((B + 1) // 2, dtype=torch.uint8, device=dev) if compact else None)
         d["desc"] = mg.TensorDesc(wl.n, wl.m, spec.rows, spec.cols, 0, spec.tensor_id)
         d["B"] = B
         bufs.append(d)
@@ -97,11 +99,12 @@ def main():
     total_blocks = sum(d["B"] for d in bufs)
     torch.cuda.synchronize()
 
-    bf = mg.MASKGS_BF16
+    bf = mg.MASKGS_BF16 if wl.w_dtype == "bf16" else mg.MASKGS_F32
+    gdt = mg.MASKGS_BF16 if wl.g_dtype == "bf16" else mg.MASKGS_F32
     P = ctypes.c_void_p
 
     def ptr(t):
-        return P(t.data_ptr())
+        return None if t is None else P(t.data_ptr())
 
     # pre-marshalled argument tuples: the timed loop only calls the C ABI
     calls = {"fwd": [], "bwd": [], "hard": []}
@@ -112,80 +115,96 @@ def main():
         calls["fwd"].append((L.maskgs_fwd, (dref, pref, ptr(d["w"]), bf, ptr(d["z"]), ptr(d["out"]),
                                             bf, ptr(d["y"]), ptr(reg), sptr)))
         calls["bwd"].append((L.maskgs_bwd, (dref, pref, ptr(d["w"]), bf, None, ptr(d["y"]),
-                                            ptr(d["G"]), bf, ctypes.c_float(wl.lam), ptr(d["dz"]), 0,
+                                            ptr(d["G"]), gdt, ctypes.c_float(wl.lam), ptr(d["dz"]), 0,
                                             sptr)))
         calls["hard"].append((L.maskgs_hard_extract, (dref, ptr(d["z"]), ptr(d["w"]), bf, None,
                                                        ptr(d["bits"]), ptr(d["vals"]),
                                                        ptr(d["vidx"]), sptr)))
 
-    ev = {k: [] for k in calls}
+    # per-block algorithmic bytes of each kernel (bf16 weights, fp32 logits)
+    K, M, N = wl.k, wl.m, wl.n
+    wb = 2 if wl.w_dtype == "bf16" else 4
+    per_block_bytes = {
+        "fwd": M * wb + 4 * K + M * 2 + 4 * K,            # W, z in; W.M (bf16), y out
+        "bwd": M * wb + M * 2 + 4 * K + 4 * K,            # W, G, y in; dz out
+        "hard": 4 * K + M / 8 + ((M * wb + N * wb + 0.5) if (N, M) == (2, 4) else 0.0),
+    }
+    big = [i for i, d in enumerate(bufs) if d["B"] == max(x["B"] for x in bufs)]
+    phase = {k: [] for k in calls}
+    launch_ev = {k: [] for k in calls}
 
-    def step(record: bool):
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def step(timed_kind=None):
+        """One step.  Phase events bracket each kernel kind; per-launch events
+        are recorded only around the launches of `timed_kind` on the largest
+        tensors (the launch shape the roofline reports)."""
         reg.zero_()
         for kind in ("fwd", "bwd", "hard"):
-            for fn, a in calls[kind]:
-                if record:
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
+            p0, p1 = ev(), ev()
+            p0.record(stream)
+            for i, (fn, a) in enumerate(calls[kind]):
+                rec = kind == timed_kind and i in big_set
+                if rec:
+                    e0, e1 = ev(), ev()
                     e0.record(stream)
                 rc = fn(*a)
                 if rc != 0:
                     raise RuntimeError(f"{kind}: status {rc}")
-                if record:
+                if rec:
                     e1.record(stream)
-                    ev[kind].append((e0, e1))
+                    launch_ev[kind].append((e0, e1))
+            p1.record(stream)
+            phase[kind].append((p0, p1))
 
+    big_set = set(big)
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
+    # the dominant kernel (largest share of a step) is chosen from the warmup
+    # phases; its launches on the largest tensors are timed in the timed steps
+    warm = {k: sum(a.elapsed_time(b) for a, b in v) for k, v in phase.items()}
+    dom = max(warm, key=warm.get) if args.warmup else "fwd"
+    for v in phase.values():
+        v.clear()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for s in range(args.steps):
         params[0].step = s
-        step(True)
+        step(dom)
     t1.record(stream)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
 
     # ---- per-kernel statistics (HIP events on the launch stream) ----------
-    per_block_bytes = {"fwd": 8 + 24 + 8 + 24, "bwd": 8 + 24 + 8 + 24,
-                       "hard": 24 + 8 + 0.5 + 4 + 0.5}
     kstats = {}
-    for kind, pairs in ev.items():
-        times = [a.elapsed_time(b) for a, b in pairs]
-        tot = sum(times) / args.steps
-        # the largest tensor class dominates; report an average over all launches
-        nl = len(pairs) // args.steps
-        avg_us = 1e3 * sum(times) / len(times)
+    for kind, pairs in phase.items():
+        tot = sum(a.elapsed_time(b) for a, b in pairs) / args.steps
         bytes_per_step = per_block_bytes[kind] * total_blocks
-        kstats[kind] = dict(ms_per_step=round(tot, 4), launches_per_step=nl,
-                            avg_launch_us=round(avg_us, 2),
+        kstats[kind] = dict(ms_per_step=round(tot, 4), launches_per_step=len(calls[kind]),
                             algorithmic_bytes_per_block=per_block_bytes[kind],
                             achieved_gbs=round(bytes_per_step / (tot * 1e-3) / 1e9, 1))
-    dom = max(kstats, key=lambda k: kstats[k]["ms_per_step"])
-
-    # roofline of the dominant kernel: one launch on the largest tensors
-    # (11008x4096, 11.27M blocks) -- the launch shape profiled by rocprofv3
-    big = [i for i, d in enumerate(bufs) if d["B"] == max(x["B"] for x in bufs)]
-    nl = len(bufs)
-    big_times = [ev[dom][s * nl + i][0].elapsed_time(ev[dom][s * nl + i][1])
-                 for s in range(args.steps) for i in big]
+    big_times = [a.elapsed_time(b) for a, b in launch_ev[dom]]
     big_ms = sum(big_times) / len(big_times)
-    big_bytes = per_block_bytes[dom] * bufs[big[0]]["B"]
+    big_blocks = bufs[big[0]]["B"]
+    big_bytes = per_block_bytes[dom] * big_blocks
     achieved = big_bytes / (big_ms * 1e-3) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         k = tr.get("kernels", {}).get(dom)
-        if k and tr.get("source_hash") == source_hash():
+        if k and tr.get("source_hash") == source_hash() and tr.get("workload") == wl.key:
             traffic = k.get("hbm_bytes_per_launch")
-    roofline = dict(bound="hbm", kernel=f"maskgs_{dom} (2:4, 11008x4096 bf16 tensor)",
+    spec = bufs[big[0]]["spec"]
+    roofline = dict(bound="hbm", kernel=f"maskgs_{dom} ({wl.n}:{wl.m}, {spec.rows}x{spec.cols} "
+                    f"{wl.w_dtype} tensor, {big_blocks} blocks)",
                     achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
-                    avg_launch_us=round(big_ms * 1e3, 2),
+                    avg_launch_us=round(big_ms * 1e3, 2), launches_timed=len(big_times),
                     algorithmic_bytes_per_launch=int(big_bytes))
 
     # ---- prior seeding, timed once (initialisation row of the path) -------
@@ -209,8 +228,10 @@ def main():
         del a, b
 
     fwd_bwd_ms = kstats["fwd"]["ms_per_step"] + kstats["bwd"]["ms_per_step"]
+    fb_bytes = per_block_bytes["fwd"] + per_block_bytes["bwd"]
     result = {
-        "metric": "weight-blocks/s and HBM GB/s (% of peak), 2:4 mask fwd+bwd, LLaMA-2-7B shapes",
+        "metric": (f"weight-blocks/s and HBM GB/s (% of peak), {wl.n}:{wl.m} mask fwd+bwd, "
+                   f"{'LLaMA-2-7B' if wl.key.startswith('llama') else 'Nemotron-4-15B'} shapes"),
         "value": round(total_blocks / (ms_step * 1e-3), 1),
         "unit": "weight-blocks/s",
         "n_gpus": 1,
@@ -223,16 +244,17 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.key, "tensors": len(bufs), "blocks": total_blocks,
-                   "n_m": f"{wl.n}:{wl.m}", "weights": "bf16 N(0,0.02)",
-                   "logits": "fp32 N(0,1)", "upstream_grad": "bf16 N(0,1e-3)",
+                   "n_m": f"{wl.n}:{wl.m}", "weights": f"{wl.w_dtype} N(0,{wl.w_std})",
+                   "logits": f"fp32 N(0,{wl.z_std})", "upstream_grad": f"{wl.g_dtype} N(0,{wl.g_std})",
                    "kappa": wl.kappa, "tau": wl.tau, "lambda": wl.lam,
                    "step": "fwd (y saved, reg) + bwd (saved y) + hard extract/pack/compact",
                    "parallelism": "single GPU"},
         "fwd_bwd_blocks_per_s": round(total_blocks / (fwd_bwd_ms * 1e-3), 1),
-        "fwd_bwd_hbm_gbs": round(128 * total_blocks / (fwd_bwd_ms * 1e-3) / 1e9, 1),
+        "fwd_bwd_hbm_gbs": round(fb_bytes * total_blocks / (fwd_bwd_ms * 1e-3) / 1e9, 1),
         "kernels": kstats,
         "prior_init": {"ms_all_tensors": round(prior_ms, 3),
-                       "achieved_gbs": round(56 * total_blocks / (prior_ms * 1e-3) / 1e9, 1)},
+                       "achieved_gbs": round((M * wb + 8 * K) * total_blocks / (prior_ms * 1e-3) / 1e9,
+                                             1)},
         "roofline": roofline,
     }
 
@@ -264,13 +286,14 @@ def cpu_baseline(wl, bufs, mg):
         t = time.perf_counter()
         oracle.fwd(wl.n, wl.m, wf, zf, **kw)
         oracle.bwd(wl.n, wl.m, wf, zf, gf, lam=wl.lam, **kw)
-        oracle.hard_extract(wl.n, wl.m, zf, spec.rows, spec.cols, w_raw=wu)
+        oracle.hard_extract(wl.n, wl.m, zf, spec.rows, spec.cols,
+                            w_raw=wu if (wl.n, wl.m) == (2, 4) else None)
         secs += time.perf_counter() - t
         blocks += d["B"]
         del wu, wf, zf, gf
     return {"value": round(blocks / secs, 1), "unit": "weight-blocks/s", "cores": used,
             "kind": "oracle",
-            "sample": f"layer 0 of the same workload ({len(sample)} tensors, {blocks} blocks): "
+            "sample": f"first layer of the same workload ({len(sample)} tensors, {blocks} blocks): "
                       f"fwd + bwd + hard extract, {secs:.1f} s of CPU time"}
 
 

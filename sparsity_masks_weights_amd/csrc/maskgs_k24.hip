@@ -18,8 +18,14 @@
 namespace maskgs {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWavesPerCU = 8;  // grid cap: 8 workgroups of 256 per CU
+#ifndef MASKGS_K24_THREADS
+#define MASKGS_K24_THREADS 512
+#endif
+constexpr int kThreads = MASKGS_K24_THREADS;
+#ifndef MASKGS_K24_WG_PER_CU
+#define MASKGS_K24_WG_PER_CU 8
+#endif
+constexpr int kWavesPerCU = MASKGS_K24_WG_PER_CU;  // grid cap: workgroups of 256 per CU
 using C24 = Cands<2, 4>;
 
 // ---------------------------------------------------------------------------
@@ -446,8 +452,11 @@ __global__ __launch_bounds__(kThreads) void hard24_kernel(HardArgs a) {
     for (int64_t p = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; p < npairs;
          p += stride) {
         const bool two = 2 * p + 1 < a.g.nblocks;
+        // both streams are requested before any use, so their latencies overlap
         float z[12];
+        uint32_t r[8];
         load12(a.z, p, two, z);
+        if (a.values) Io<WT>::load8_raw(a.w, p, two, r);
         const int k0 = first_argmax6(z), k1 = first_argmax6(z + 6);
         const uint32_t m0 = cand_mask6(k0), m1 = two ? cand_mask6(k1) : 0u;
         if (a.idx) {
@@ -464,8 +473,6 @@ __global__ __launch_bounds__(kThreads) void hard24_kernel(HardArgs a) {
             a.val_idx[p] = static_cast<uint8_t>((lo0 | (hi0 << 2)) |
                                                 (two ? ((lo1 | (hi1 << 2)) << 4) : 0u));
         if (a.values) {
-            uint32_t r[8];
-            Io<WT>::load8_raw(a.w, p, two, r);
             const uint32_t v[4] = {pick4(r, lo0), pick4(r, hi0), pick4(r + 4, lo1),
                                    pick4(r + 4, hi1)};
             Io<WT>::store_values(a.values, p, two, v);
