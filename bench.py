@@ -3,10 +3,12 @@
 One step = one pass of the hot path over every linear weight of a 32-layer
 LLaMA-2-7B-shaped model (224 tensors, 1.62e9 2:4 blocks, inputs resident in
 HBM): the Gumbel soft-mask forward of every tensor (W (.) M~ in bf16, soft
-index saved, regulariser reduced), then the logit backward of every tensor
-(from the saved soft index), then hard-mask extraction with bit packing and
-2:4 compaction of every tensor.  Prior seeding, an initialisation step, is
-timed once after the steps and reported beside them.
+index saved, regulariser reduced) with the hard mask of the same logits
+(argmax, bit packing, 2:4 values and 2-bit indices) produced in the same pass,
+then the logit backward of every tensor (from the saved soft index).  The
+step's outputs equal those of forward, backward and a separate extraction
+pass; that unfused order is timed too and reported beside the step.  Prior
+seeding, an initialisation step, is timed once after the steps.
 
 Prints ONE JSON line.  `value` = 2:4 weight blocks per second through the whole
 step; `roofline` describes the kernel with the largest share of the step;
@@ -108,6 +110,7 @@ def main():
 
     # pre-marshalled argument tuples: the timed loop only calls the C ABI
     calls = {"fwd": [], "bwd": [], "hard": []}
+    fused = []
     params = [mg.SampleParams(0, 0, wl.kappa, wl.tau, 0)]
     pref = ctypes.byref(params[0])
     for d in bufs:
@@ -120,28 +123,41 @@ def main():
         calls["hard"].append((L.maskgs_hard_extract, (dref, ptr(d["z"]), ptr(d["w"]), bf, None,
                                                        ptr(d["bits"]), ptr(d["vals"]),
                                                        ptr(d["vidx"]), sptr)))
+        fused.append((L.maskgs_fwd_hard, (dref, pref, ptr(d["w"]), bf, ptr(d["z"]), ptr(d["out"]),
+                                          bf, ptr(d["y"]), ptr(reg), None, ptr(d["bits"]),
+                                          ptr(d["vals"]), ptr(d["vidx"]), sptr)))
 
     # per-block algorithmic bytes of each kernel (bf16 weights, fp32 logits)
     K, M, N = wl.k, wl.m, wl.n
     wb = 2 if wl.w_dtype == "bf16" else 4
+    hard_out = M / 8 + ((N * wb + 0.5) if compact else 0.0)   # bits (+ values, indices)
     per_block_bytes = {
         "fwd": M * wb + 4 * K + M * 2 + 4 * K,            # W, z in; W.M (bf16), y out
+        "fwd_hard": M * wb + 4 * K + M * 2 + 4 * K + hard_out,
         "bwd": M * wb + M * 2 + 4 * K + 4 * K,            # W, G, y in; dz out
-        "hard": 4 * K + M / 8 + ((M * wb + N * wb + 0.5) if (N, M) == (2, 4) else 0.0),
+        "hard": 4 * K + (M * wb if compact else 0) + hard_out,
     }
+    calls["fwd_hard"] = fused
     big = [i for i, d in enumerate(bufs) if d["B"] == max(x["B"] for x in bufs)]
+    big_set = set(big)
+    # The step: the forward of every tensor with the hard mask of the same
+    # logits fused in (one read of z and W), then the backward of every tensor.
+    # Outputs are bit-identical to forward, backward, then extraction (z is not
+    # written by the step); that unfused order is timed after the timed steps.
+    fused_kinds = ("fwd_hard", "bwd")
+    unfused_kinds = ("fwd", "bwd", "hard")
     phase = {k: [] for k in calls}
     launch_ev = {k: [] for k in calls}
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    def step(timed_kind=None):
+    def step(kinds, timed_kind=None):
         """One step.  Phase events bracket each kernel kind; per-launch events
         are recorded only around the launches of `timed_kind` on the largest
         tensors (the launch shape the roofline reports)."""
         reg.zero_()
-        for kind in ("fwd", "bwd", "hard"):
+        for kind in kinds:
             p0, p1 = ev(), ev()
             p0.record(stream)
             for i, (fn, a) in enumerate(calls[kind]):
@@ -158,14 +174,13 @@ def main():
             p1.record(stream)
             phase[kind].append((p0, p1))
 
-    big_set = set(big)
     for _ in range(args.warmup):
-        step()
+        step(fused_kinds)
     torch.cuda.synchronize()
     # the dominant kernel (largest share of a step) is chosen from the warmup
     # phases; its launches on the largest tensors are timed in the timed steps
-    warm = {k: sum(a.elapsed_time(b) for a, b in v) for k, v in phase.items()}
-    dom = max(warm, key=warm.get) if args.warmup else "fwd"
+    warm = {k: sum(a.elapsed_time(b) for a, b in v) for k, v in phase.items() if v}
+    dom = max(warm, key=warm.get) if args.warmup else "fwd_hard"
     for v in phase.values():
         v.clear()
     t0 = torch.cuda.Event(enable_timing=True)
@@ -174,19 +189,24 @@ def main():
     t0.record(stream)
     for s in range(args.steps):
         params[0].step = s
-        step(dom)
+        step(fused_kinds, dom)
     t1.record(stream)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
 
     # ---- per-kernel statistics (HIP events on the launch stream) ----------
-    kstats = {}
-    for kind, pairs in phase.items():
-        tot = sum(a.elapsed_time(b) for a, b in pairs) / args.steps
-        bytes_per_step = per_block_bytes[kind] * total_blocks
-        kstats[kind] = dict(ms_per_step=round(tot, 4), launches_per_step=len(calls[kind]),
-                            algorithmic_bytes_per_block=per_block_bytes[kind],
-                            achieved_gbs=round(bytes_per_step / (tot * 1e-3) / 1e9, 1))
+    def kernel_stats(kinds, nsteps):
+        out = {}
+        for kind in kinds:
+            pairs = phase[kind]
+            tot = sum(a.elapsed_time(b) for a, b in pairs) / nsteps
+            bytes_per_step = per_block_bytes[kind] * total_blocks
+            out[kind] = dict(ms_per_step=round(tot, 4), launches_per_step=len(calls[kind]),
+                             algorithmic_bytes_per_block=per_block_bytes[kind],
+                             achieved_gbs=round(bytes_per_step / (tot * 1e-3) / 1e9, 1))
+        return out
+
+    kstats = kernel_stats(fused_kinds, args.steps)
     big_times = [a.elapsed_time(b) for a, b in launch_ev[dom]]
     big_ms = sum(big_times) / len(big_times)
     big_blocks = bufs[big[0]]["B"]
@@ -206,6 +226,20 @@ def main():
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                     avg_launch_us=round(big_ms * 1e3, 2), launches_timed=len(big_times),
                     algorithmic_bytes_per_launch=int(big_bytes))
+
+    # ---- the unfused order (forward, backward, extraction), for reference --
+    for v in phase.values():
+        v.clear()
+    u0, u1 = ev(), ev()
+    torch.cuda.synchronize()
+    u0.record(stream)
+    for s in range(args.steps):
+        params[0].step = s
+        step(unfused_kinds)
+    u1.record(stream)
+    torch.cuda.synchronize()
+    ms_unfused = u0.elapsed_time(u1) / args.steps
+    ustats = kernel_stats(unfused_kinds, args.steps)
 
     # ---- prior seeding, timed once (initialisation row of the path) -------
     pe0 = torch.cuda.Event(enable_timing=True)
@@ -227,7 +261,7 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    fwd_bwd_ms = kstats["fwd"]["ms_per_step"] + kstats["bwd"]["ms_per_step"]
+    fwd_bwd_ms = ustats["fwd"]["ms_per_step"] + ustats["bwd"]["ms_per_step"]
     fb_bytes = per_block_bytes["fwd"] + per_block_bytes["bwd"]
     result = {
         "metric": (f"weight-blocks/s and HBM GB/s (% of peak), {wl.n}:{wl.m} mask fwd+bwd, "
@@ -247,11 +281,16 @@ def main():
                    "n_m": f"{wl.n}:{wl.m}", "weights": f"{wl.w_dtype} N(0,{wl.w_std})",
                    "logits": f"fp32 N(0,{wl.z_std})", "upstream_grad": f"{wl.g_dtype} N(0,{wl.g_std})",
                    "kappa": wl.kappa, "tau": wl.tau, "lambda": wl.lam,
-                   "step": "fwd (y saved, reg) + bwd (saved y) + hard extract/pack/compact",
+                   "step": "fwd (y saved, reg) with the hard mask of the same logits fused in "
+                           "(argmax, bit-pack, 2:4 compaction) + bwd (saved y)",
                    "parallelism": "single GPU"},
-        "fwd_bwd_blocks_per_s": round(total_blocks / (fwd_bwd_ms * 1e-3), 1),
+        "fwd_bwd_blocks_per_s": round(total_blocks / (fwd_bwd_ms * 1e-3), 1),  # unfused fwd + bwd
         "fwd_bwd_hbm_gbs": round(fb_bytes * total_blocks / (fwd_bwd_ms * 1e-3) / 1e9, 1),
         "kernels": kstats,
+        "unfused_step": {"order": "fwd, bwd, then hard extract (separate pass over z and W)",
+                         "ms_per_step": round(ms_unfused, 3),
+                         "value": round(total_blocks / (ms_unfused * 1e-3), 1),
+                         "kernels": ustats},
         "prior_init": {"ms_all_tensors": round(prior_ms, 3),
                        "achieved_gbs": round((M * wb + 8 * K) * total_blocks / (prior_ms * 1e-3) / 1e9,
                                              1)},

@@ -117,6 +117,18 @@ int maskgs_fwd(const maskgs_tensor_desc *t, const maskgs_sample_params *p, const
                maskgs_dtype w_dt, const float *z, void *out, maskgs_dtype out_dt, float *y_save,
                double *reg_accum, hipStream_t stream);
 
+/* Forward plus the hard mask of the same logits: the outputs of maskgs_fwd and
+ * those of maskgs_hard_extract on z (idx, mask_bits, and for 2:4 values and
+ * val_idx, each NULL to skip; formats as documented there), bit-identical to
+ * the two calls in sequence, with z and w read once.  The per-step hard mask
+ * is what the mask-change and maximum-probability diagnostics of section 3.4
+ * (kappa sweep, Figure 5) track during training.  values/val_idx for 4:8
+ * return MASKGS_E_UNSUPPORTED. */
+int maskgs_fwd_hard(const maskgs_tensor_desc *t, const maskgs_sample_params *p, const void *w,
+                    maskgs_dtype w_dt, const float *z, void *out, maskgs_dtype out_dt,
+                    float *y_save, double *reg_accum, uint8_t *idx, uint8_t *mask_bits,
+                    void *values, uint8_t *val_idx, hipStream_t stream);
+
 /* Backward to the logits (section 3.2 information flow; section 3.4 Eq. 8).
  * With G = dL_LM/d(W (.) M~) and W frozen, the gradient of
  * L = L_LM - lambda * sum_b ||W_b (.) M~_b||^2 is, per block,

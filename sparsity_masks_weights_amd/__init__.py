@@ -34,6 +34,7 @@ MASKGS_BF16 = 1
 MASKGS_NO_NOISE = 1
 
 EXPORTS = ("maskgs_abi_version", "maskgs_status_str", "maskgs_candidates", "maskgs_fwd",
+           "maskgs_fwd_hard",
            "maskgs_bwd", "maskgs_reg_reduce", "maskgs_hard_extract", "maskgs_prior_init",
            "maskgs_debug_philox", "maskgs_debug_gumbel")
 
@@ -78,6 +79,7 @@ def load_library(path: str = LIB_PATH):
     L.maskgs_status_str.restype = c.c_char_p
     L.maskgs_candidates.argtypes = [c.c_int32, c.c_int32, P, c.c_int32, c.POINTER(c.c_int32)]
     L.maskgs_fwd.argtypes = [DP, SP, P, c.c_int, P, P, c.c_int, P, P, P]
+    L.maskgs_fwd_hard.argtypes = [DP, SP, P, c.c_int, P, P, c.c_int, P, P, P, P, P, P, P]
     L.maskgs_bwd.argtypes = [DP, SP, P, c.c_int, P, P, P, c.c_int, c.c_float, P, c.c_int32, P]
     L.maskgs_reg_reduce.argtypes = [DP, SP, P, c.c_int, P, P, P, P]
     L.maskgs_hard_extract.argtypes = [DP, P, P, c.c_int, P, P, P, P, P]
@@ -193,6 +195,26 @@ def maskgs_fwd(t: Tensor, p: SampleParams, w, z, out, y_save=None, reg_accum=Non
         _ptr(out, "out", numel=t.rows * t.cols, device=dev), _dtype_code(out),
         _ptr(y_save, "y_save", _torch().float32, t.nblocks * t.k, dev),
         _ptr(reg_accum, "reg_accum", _torch().float64, 1, dev), _stream(stream)))
+    return out
+
+
+def maskgs_fwd_hard(t: Tensor, p: SampleParams, w, z, out, y_save=None, reg_accum=None,
+                    idx=None, mask_bits=None, values=None, val_idx=None, stream=None):
+    """maskgs_fwd plus the hard mask of the same logits (z read once)."""
+    torch = _torch()
+    dev = w.device
+    B = t.nblocks
+    _check("maskgs_fwd_hard", load_library().maskgs_fwd_hard(
+        ctypes.byref(t.desc()), ctypes.byref(p),
+        _ptr(w, "w", numel=t.rows * t.cols, device=dev), _dtype_code(w),
+        _ptr(z, "z", torch.float32, B * t.k, dev),
+        _ptr(out, "out", numel=t.rows * t.cols, device=dev), _dtype_code(out),
+        _ptr(y_save, "y_save", torch.float32, B * t.k, dev),
+        _ptr(reg_accum, "reg_accum", torch.float64, 1, dev),
+        _ptr(idx, "idx", torch.uint8, B, dev),
+        _ptr(mask_bits, "mask_bits", torch.uint8, (B * t.m + 7) // 8, dev),
+        _ptr(values, "values", w.dtype, B * t.n, dev),
+        _ptr(val_idx, "val_idx", torch.uint8, (B + 1) // 2, dev), _stream(stream)))
     return out
 
 

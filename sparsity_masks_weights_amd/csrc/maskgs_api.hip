@@ -133,6 +133,28 @@ int maskgs_fwd(const maskgs_tensor_desc *t, const maskgs_sample_params *p, const
     return launch_status(launch_fwd48(a, w_dt, out_dt, stream));
 }
 
+int maskgs_fwd_hard(const maskgs_tensor_desc *t, const maskgs_sample_params *p, const void *w,
+                    maskgs_dtype w_dt, const float *z, void *out, maskgs_dtype out_dt,
+                    float *y_save, double *reg_accum, uint8_t *idx, uint8_t *mask_bits,
+                    void *values, uint8_t *val_idx, hipStream_t stream) {
+    Geometry g;
+    Noise nz;
+    int rc = check_desc(t, &g);
+    if (rc) return rc;
+    if ((rc = check_params(p, &nz))) return rc;
+    if ((values || val_idx) && g.m != 4) return MASKGS_E_UNSUPPORTED;
+    if (g.nblocks == 0) return MASKGS_OK;
+    if (!w || !z || !out) return MASKGS_E_NULL;
+    if (!valid_dtype(w_dt) || !valid_dtype(out_dt)) return MASKGS_E_DTYPE;
+    if (misaligned(w) || misaligned(z) || misaligned(out) || misaligned(y_save) ||
+        misaligned(reg_accum) || misaligned(idx) || misaligned(mask_bits) || misaligned(values) ||
+        misaligned(val_idx))
+        return MASKGS_E_ALIGN;
+    FwdArgs a{w, z, out, y_save, reg_accum, g, nz, idx, mask_bits, values, val_idx};
+    if (g.m == 4) return launch_status(launch_fwd24(a, w_dt, out_dt, stream));
+    return launch_status(launch_fwd48(a, w_dt, out_dt, stream));
+}
+
 int maskgs_bwd(const maskgs_tensor_desc *t, const maskgs_sample_params *p, const void *w,
                maskgs_dtype w_dt, const float *z, const float *y_saved, const void *dout,
                maskgs_dtype dout_dt, float lambda, float *dz, int32_t accumulate,

@@ -81,6 +81,8 @@ struct Io<bf16_t> {
         }
     }
     static __device__ __forceinline__ uint32_t magnitude(uint32_t raw) { return raw & 0x7FFFu; }
+    // bit pattern of a value that was widened from bf16 (exact)
+    static __device__ __forceinline__ uint32_t raw_of(float v) { return __float_as_uint(v) >> 16; }
     static __device__ __forceinline__ void store8(void *base, int64_t p, bool two,
                                                   const float (&v)[8]) {
         uint16_t *ptr = static_cast<uint16_t *>(base) + p * 8;
@@ -130,6 +132,7 @@ struct Io<float> {
     static __device__ __forceinline__ uint32_t magnitude(uint32_t raw) {
         return raw & 0x7FFFFFFFu;
     }
+    static __device__ __forceinline__ uint32_t raw_of(float v) { return __float_as_uint(v); }
     static __device__ __forceinline__ void store8(void *base, int64_t p, bool two,
                                                   const float (&v)[8]) {
         float *ptr = static_cast<float *>(base) + p * 8;
@@ -232,6 +235,65 @@ __device__ __forceinline__ void soft_mask4(const float *y, float *m) {
     }
 }
 
+// Hard mask (section 3.2 inference flow; Algorithm 1 step 3): first index of
+// the largest logit, its candidate mask, kept positions and values.
+__device__ __forceinline__ int first_argmax6(const float *z) {
+    int best = 0;
+    float bv = z[0];
+#pragma unroll
+    for (int i = 1; i < 6; ++i)
+        if (z[i] > bv) {
+            bv = z[i];
+            best = i;
+        }
+    return best;
+}
+
+// The six candidate masks packed as nibbles (nibble i = mask i), so that a
+// runtime candidate index selects its mask with one shift.
+constexpr uint32_t pack_nibbles24() {
+    uint32_t v = 0;
+    for (int i = 0; i < 6; ++i) v |= static_cast<uint32_t>(C24::mask[i]) << (4 * i);
+    return v;
+}
+constexpr uint32_t kMaskNibbles24 = pack_nibbles24();
+
+__device__ __forceinline__ uint32_t cand_mask6(int k) { return (kMaskNibbles24 >> (4 * k)) & 0xFu; }
+
+// Selects among four register values without indexing an array (which would
+// place the array in scratch memory).
+__device__ __forceinline__ uint32_t pick4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
+                                          uint32_t pos) {
+    return pos == 0 ? r0 : pos == 1 ? r1 : pos == 2 ? r2 : r3;
+}
+
+// Hard mask of one pair from its logits z and raw weight bits r (r read only
+// when values are requested).
+template <typename WT>
+__device__ __forceinline__ void hard_pair(uint8_t *idx, uint8_t *bits, void *values,
+                                          uint8_t *val_idx, int64_t p, bool two,
+                                          const float (&z)[12], const uint32_t (&r)[8]) {
+    const int k0 = first_argmax6(z), k1 = first_argmax6(z + 6);
+    const uint32_t m0 = cand_mask6(k0), m1 = two ? cand_mask6(k1) : 0u;
+    if (idx) {
+        if (two)
+            *reinterpret_cast<uint16_t *>(idx + 2 * p) = static_cast<uint16_t>(k0 | (k1 << 8));
+        else
+            idx[2 * p] = static_cast<uint8_t>(k0);
+    }
+    if (bits) bits[p] = static_cast<uint8_t>(m0 | (m1 << 4));
+    const uint32_t lo0 = __builtin_ctz(m0), hi0 = 31 - __builtin_clz(m0);
+    const uint32_t lo1 = two ? __builtin_ctz(m1) : 0u, hi1 = two ? 31 - __builtin_clz(m1) : 0u;
+    if (val_idx)
+        val_idx[p] = static_cast<uint8_t>((lo0 | (hi0 << 2)) |
+                                          (two ? ((lo1 | (hi1 << 2)) << 4) : 0u));
+    if (values) {
+        const uint32_t v[4] = {pick4(r[0], r[1], r[2], r[3], lo0), pick4(r[0], r[1], r[2], r[3], hi0),
+                               pick4(r[4], r[5], r[6], r[7], lo1), pick4(r[4], r[5], r[6], r[7], hi1)};
+        Io<WT>::store_values(values, p, two, v);
+    }
+}
+
 // Soft index of a pair (section 3.4, Eq. 6 and Algorithm 1 steps 1-2):
 // a_i = fp32(fp32(kappa z_i + g_i) * fp32(1/tau)) with g the contract noise.
 // The noise flag is uniform, so the twelve Gumbel evaluations form one
@@ -276,6 +338,7 @@ __device__ __forceinline__ void reduce_add(double v, double *dst) {
 template <int PHASE, typename WT, typename OT>
 __global__ __launch_bounds__(kThreads) void fwd24_kernel(FwdArgs a) {
     __shared__ float4 stage[3 * kThreads];
+    const bool hard = a.idx || a.bits || a.values || a.val_idx;
     const int64_t npairs = (a.g.nblocks + 1) >> 1;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
     double reg = 0.0;
@@ -288,6 +351,13 @@ __global__ __launch_bounds__(kThreads) void fwd24_kernel(FwdArgs a) {
             float w[8], z[12], out[8];
             Io<WT>::load8(a.w, p, two, w);
             load12(a.z, p, two, z);
+            if (hard) {
+                // hard mask of the same logits (argmax of z, not of the sample)
+                uint32_t r[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) r[j] = Io<WT>::raw_of(w[j]);
+                hard_pair<WT>(a.idx, a.bits, a.values, a.val_idx, p, two, z, r);
+            }
             pair_soft_index<PHASE>(a, p, z, y);
             float racc = 0.0f;
 #pragma unroll
@@ -416,35 +486,8 @@ __global__ __launch_bounds__(kThreads) void reg24_kernel(RegArgs a) {
 
 // ---------------------------------------------------------------------------
 // Hard mask: argmax, packed bits, 2:4 values and 2-bit indices (section 3.2
-// inference flow; Algorithm 1 step 3).
+// inference flow; Algorithm 1 step 3), as a pass of its own.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int first_argmax6(const float *z) {
-    int best = 0;
-    float bv = z[0];
-#pragma unroll
-    for (int i = 1; i < 6; ++i)
-        if (z[i] > bv) {
-            bv = z[i];
-            best = i;
-        }
-    return best;
-}
-
-// The six candidate masks packed as nibbles (nibble i = mask i), so that a
-// runtime candidate index selects its mask with one shift.
-constexpr uint32_t pack_nibbles24() {
-    uint32_t v = 0;
-    for (int i = 0; i < 6; ++i) v |= static_cast<uint32_t>(C24::mask[i]) << (4 * i);
-    return v;
-}
-constexpr uint32_t kMaskNibbles24 = pack_nibbles24();
-
-__device__ __forceinline__ uint32_t cand_mask6(int k) { return (kMaskNibbles24 >> (4 * k)) & 0xFu; }
-
-__device__ __forceinline__ uint32_t pick4(const uint32_t *r, uint32_t pos) {
-    return pos == 0 ? r[0] : pos == 1 ? r[1] : pos == 2 ? r[2] : r[3];
-}
-
 template <typename WT>
 __global__ __launch_bounds__(kThreads) void hard24_kernel(HardArgs a) {
     const int64_t npairs = (a.g.nblocks + 1) >> 1;
@@ -454,29 +497,10 @@ __global__ __launch_bounds__(kThreads) void hard24_kernel(HardArgs a) {
         const bool two = 2 * p + 1 < a.g.nblocks;
         // both streams are requested before any use, so their latencies overlap
         float z[12];
-        uint32_t r[8];
+        uint32_t r[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
         load12(a.z, p, two, z);
         if (a.values) Io<WT>::load8_raw(a.w, p, two, r);
-        const int k0 = first_argmax6(z), k1 = first_argmax6(z + 6);
-        const uint32_t m0 = cand_mask6(k0), m1 = two ? cand_mask6(k1) : 0u;
-        if (a.idx) {
-            if (two)
-                *reinterpret_cast<uint16_t *>(a.idx + 2 * p) =
-                    static_cast<uint16_t>(k0 | (k1 << 8));
-            else
-                a.idx[2 * p] = static_cast<uint8_t>(k0);
-        }
-        if (a.bits) a.bits[p] = static_cast<uint8_t>(m0 | (m1 << 4));
-        const uint32_t lo0 = __builtin_ctz(m0), hi0 = 31 - __builtin_clz(m0);
-        const uint32_t lo1 = two ? __builtin_ctz(m1) : 0u, hi1 = two ? 31 - __builtin_clz(m1) : 0u;
-        if (a.val_idx)
-            a.val_idx[p] = static_cast<uint8_t>((lo0 | (hi0 << 2)) |
-                                                (two ? ((lo1 | (hi1 << 2)) << 4) : 0u));
-        if (a.values) {
-            const uint32_t v[4] = {pick4(r, lo0), pick4(r, hi0), pick4(r + 4, lo1),
-                                   pick4(r + 4, hi1)};
-            Io<WT>::store_values(a.values, p, two, v);
-        }
+        hard_pair<WT>(a.idx, a.bits, a.values, a.val_idx, p, two, z, r);
     }
 }
 

@@ -273,6 +273,21 @@ __global__ __launch_bounds__(kWave) void fwd48_kernel(FwdArgs a) {
         float v[kK];
         tile_in<false>(a.z, b0, nb, stage, v);
         if (lane < nb) {
+            if (a.idx || a.bits) {
+                // hard mask of the same logits (argmax of z, not of the sample)
+                int best = 0;
+                float bv = v[0];
+                uint32_t mask = C48::at(0);
+#pragma unroll
+                for (int i = 1; i < kK; ++i)
+                    if (v[i] > bv) {
+                        bv = v[i];
+                        best = i;
+                        mask = C48::at(i);
+                    }
+                if (a.idx) a.idx[b] = static_cast<uint8_t>(best);
+                if (a.bits) a.bits[b] = static_cast<uint8_t>(mask);
+            }
             logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz);
             softmax70(v);
             float m[8], w[8], out[8];

@@ -35,6 +35,11 @@ struct FwdArgs {
     double *reg;  // nullable
     Geometry g;
     Noise nz;
+    // hard mask of the same logits (maskgs_fwd_hard), all nullable
+    uint8_t *idx = nullptr;
+    uint8_t *bits = nullptr;
+    void *values = nullptr;
+    uint8_t *val_idx = nullptr;
 };
 
 struct BwdArgs {

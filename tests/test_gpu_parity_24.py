@@ -270,3 +270,35 @@ def test_row_sharding_is_invariant(dev, mg):
         assert np.array_equal(part["y"], full["y"][sl])
         assert np.array_equal(part["out"], full["out"][r0:r1])
         assert np.array_equal(part["dz_s"], full["dz_s"][sl])
+
+
+@pytest.mark.parametrize("case", [CASES[1], CASES[2], CASES[4], CASES[5]])
+def test_fwd_hard_equals_fwd_then_extract(dev, mg, orc, case):
+    """The fused forward + hard mask gives bit-identical outputs to maskgs_fwd
+    followed by maskgs_hard_extract, and the oracle's."""
+    import torch
+    rows, cols, wdt, off, tid, seed, step, kappa, tau, zstd = case
+    dt = torch.float32 if wdt == "f32" else torch.bfloat16
+    w = _rand((rows, cols), 0.02, dt, dev, 1 + tid)
+    z = _rand((rows * cols // 4, 6), zstd, torch.float32, dev, 2 + tid)
+    G = _rand((rows, cols), 1e-3, dt, dev, 3 + tid)
+    t = mg.Tensor(2, 4, rows, cols, off, tid)
+    p = mg.sample_params(seed, step, kappa, tau)
+    ref = _run_all(mg, t, p, w, z, G)
+    B = t.nblocks
+    out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((B, 6), dtype=torch.float32, device=dev)
+    reg = torch.zeros(1, dtype=torch.float64, device=dev)
+    idx = torch.empty(B, dtype=torch.uint8, device=dev)
+    bits = torch.empty((B + 1) // 2, dtype=torch.uint8, device=dev)
+    vals = torch.empty(2 * B, dtype=dt, device=dev)
+    vidx = torch.empty((B + 1) // 2, dtype=torch.uint8, device=dev)
+    mg.maskgs_fwd_hard(t, p, w, z, out, y, reg, idx, bits, vals, vidx)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(out), ref["out"])
+    assert np.array_equal(to_np(y), ref["y"])
+    assert abs(reg.item() - ref["reg"]) <= 1e-12 * abs(ref["reg"])
+    for name, got in (("idx", idx), ("bits", bits), ("vals", vals), ("vidx", vidx)):
+        assert np.array_equal(to_np(got), ref[name]), name
+    h = orc.hard_extract(2, 4, to_np(z), rows, cols, w_raw=to_np(w))
+    assert np.array_equal(to_np(bits), h["bits"]) and np.array_equal(to_np(vals), h["values"])

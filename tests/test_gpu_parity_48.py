@@ -169,3 +169,28 @@ def test_nemotron_layer_sampled_rows(mg, orc):
         assert np.array_equal(to_np(bits), h["bits"]), spec.name
         del w, z, G, out, y, dz
         torch.cuda.empty_cache()
+
+
+def test_fwd_hard_48(mg, orc):
+    import torch
+    rows, cols = 37, 72
+    B = rows * cols // 8
+    w = _rand((rows, cols), 0.015, torch.bfloat16, 50)
+    z = _rand((B, K), 1.0, torch.float32, 51)
+    t = mg.Tensor(4, 8, rows, cols, 3, 4)
+    p = mg.sample_params(11, 2, 100.0, 2.0)
+    out1, out2 = (torch.empty((rows, cols), dtype=torch.bfloat16, device=w.device) for _ in range(2))
+    y1, y2 = torch.empty_like(z), torch.empty_like(z)
+    idx1, idx2 = (torch.empty(B, dtype=torch.uint8, device=w.device) for _ in range(2))
+    bits1, bits2 = (torch.empty(B, dtype=torch.uint8, device=w.device) for _ in range(2))
+    mg.maskgs_fwd(t, p, w, z, out1, y1)
+    mg.maskgs_hard_extract(t, z, None, idx1, bits1)
+    mg.maskgs_fwd_hard(t, p, w, z, out2, y2, None, idx2, bits2)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(out1), to_np(out2)) and np.array_equal(to_np(y1), to_np(y2))
+    assert np.array_equal(to_np(idx1), to_np(idx2)) and np.array_equal(to_np(bits1), to_np(bits2))
+    h = orc.hard_extract(4, 8, to_np(z), rows, cols)
+    assert np.array_equal(to_np(bits2), h["bits"]) and np.array_equal(to_np(idx2), h["idx"])
+    with pytest.raises(mg.MaskgsError):
+        mg.maskgs_fwd_hard(t, p, w, z, out2, y2, None, idx2, bits2,
+                           values=torch.empty(4 * B, dtype=torch.bfloat16, device=w.device))
