@@ -45,6 +45,29 @@ __device__ __forceinline__ int half_count(int nb, int h) {
     return c < 0 ? 0 : (c > kHalf ? kHalf : c);
 }
 
+// Copies nf floats (16-byte aligned at both ends) from global memory into LDS
+// with direct-to-LDS loads (global_load_lds_dwordx4): lane l of round k moves
+// float4 number 64k+l, so every load of the tile is in flight at once and no
+// registers stage the data.  An odd float pair at the end is moved by lane 0.
+// Follow with lds_fill_wait() and a barrier before reading the LDS copy.
+__device__ __forceinline__ void lds_fill(const float *src, float *lds, int nf) {
+    const int lane = threadIdx.x;
+    const int n4 = nf >> 2;
+    for (int k = 0; k * kWave < n4; ++k) {
+        const int i = k * kWave + lane;
+        if (i < n4)
+            __builtin_amdgcn_global_load_lds(
+                reinterpret_cast<const float4 *>(src) + i,
+                (__attribute__((address_space(3))) void *)(lds + 4 * k * kWave), 16, 0, 0);
+    }
+    if ((nf & 3) && lane == 0)
+        reinterpret_cast<float2 *>(lds)[2 * n4] = reinterpret_cast<const float2 *>(src)[2 * n4];
+}
+
+// Waits for this wave's outstanding memory operations, the direct-to-LDS
+// loads of lds_fill among them.
+__device__ __forceinline__ void lds_fill_wait() { __builtin_amdgcn_s_waitcnt(0); }
+
 template <bool ADD>
 __device__ __forceinline__ void tile_in(const float *g, int64_t b0, int nb, float *stage,
                                         float (&v)[kK]) {
@@ -52,12 +75,8 @@ __device__ __forceinline__ void tile_in(const float *g, int64_t b0, int nb, floa
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int cnt = half_count(nb, h);
-        const float *src = g + (b0 + h * kHalf) * kK;
-        const int nf = cnt * kK, n4 = nf >> 2;
-        for (int i = lane; i < n4; i += kWave)
-            reinterpret_cast<float4 *>(stage)[i] = reinterpret_cast<const float4 *>(src)[i];
-        if ((nf & 3) && lane == 0)
-            reinterpret_cast<float2 *>(stage)[2 * n4] = reinterpret_cast<const float2 *>(src)[2 * n4];
+        lds_fill(g + (b0 + h * kHalf) * kK, stage, cnt * kK);
+        lds_fill_wait();
         __syncthreads();
         const int j = lane - h * kHalf;
         if (j >= 0 && j < cnt) {
@@ -102,14 +121,9 @@ __device__ __forceinline__ void tile_out(float *g, int64_t b0, int nb, float *st
 }
 
 // Whole-tile copies (64 blocks = 17920 B, 16-byte aligned): global <-> LDS.
+// The caller waits (lds_fill_wait) and synchronises before reading.
 __device__ __forceinline__ void tile_copy_in(const float *g, int64_t b0, int nb, float *lds) {
-    const int lane = threadIdx.x;
-    const float *src = g + b0 * kK;
-    const int nf = nb * kK, n4 = nf >> 2;
-    for (int i = lane; i < n4; i += kWave)
-        reinterpret_cast<float4 *>(lds)[i] = reinterpret_cast<const float4 *>(src)[i];
-    if ((nf & 3) && lane == 0)
-        reinterpret_cast<float2 *>(lds)[2 * n4] = reinterpret_cast<const float2 *>(src)[2 * n4];
+    lds_fill(g + b0 * kK, lds, nb * kK);
 }
 
 __device__ __forceinline__ void tile_copy_out(float *g, int64_t b0, int nb, const float *lds) {
@@ -246,6 +260,28 @@ __device__ __forceinline__ void soft_mask8(const float (&y)[kK], float (&m)[8]) 
             if ((C48::at(i) >> j) & 1u) m[j] += y[i];
 }
 
+// Hard mask of a block (section 3.4, Algorithm 1 inference step): the first
+// index of the largest logit, as a strict ">" scan from i = 0 finds it, and its
+// candidate mask.  Written without per-candidate compare masks: with zmax the
+// maximum, z_i - zmax is +0 or -0 exactly when z_i equals it (subnormals are
+// kept), and the key (not_max << 15) | (i << 8) | S_i is smallest for the
+// first such i.  Returns i << 8 | S_i.
+template <typename Src>
+__device__ __forceinline__ uint32_t argmax_key70(const Src &v) {
+    float zmax = v[0];
+#pragma unroll
+    for (int i = 1; i < kK; ++i) zmax = fmaxf(zmax, v[i]);
+    uint32_t best = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < kK; ++i) {
+        const uint32_t d = __float_as_uint(v[i] - zmax) << 1;   // 0 iff equal
+        const uint32_t key = ((d < 1u ? d : 1u) << 15) | (static_cast<uint32_t>(i) << 8) |
+                             C48::at(i);
+        best = best < key ? best : key;
+    }
+    return best & 0x7FFFu;
+}
+
 __device__ __forceinline__ void reduce_add_wave(double v, double *dst) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
@@ -259,7 +295,7 @@ __device__ __forceinline__ int64_t tile_count(int64_t nblocks) {
 // ---------------------------------------------------------------------------
 // Forward (noise kernel, registers).
 // ---------------------------------------------------------------------------
-template <typename WT, typename OT>
+template <typename WT, typename OT, bool HARD>
 __global__ __launch_bounds__(kWave) void fwd48_kernel(FwdArgs a) {
     __shared__ float4 stage4[kHalf * kK / 4];
     float *stage = reinterpret_cast<float *>(stage4);
@@ -273,20 +309,11 @@ __global__ __launch_bounds__(kWave) void fwd48_kernel(FwdArgs a) {
         float v[kK];
         tile_in<false>(a.z, b0, nb, stage, v);
         if (lane < nb) {
-            if (a.idx || a.bits) {
+            if (HARD) {
                 // hard mask of the same logits (argmax of z, not of the sample)
-                int best = 0;
-                float bv = v[0];
-                uint32_t mask = C48::at(0);
-#pragma unroll
-                for (int i = 1; i < kK; ++i)
-                    if (v[i] > bv) {
-                        bv = v[i];
-                        best = i;
-                        mask = C48::at(i);
-                    }
-                if (a.idx) a.idx[b] = static_cast<uint8_t>(best);
-                if (a.bits) a.bits[b] = static_cast<uint8_t>(mask);
+                const uint32_t key = argmax_key70(v);
+                if (a.idx) a.idx[b] = static_cast<uint8_t>(key >> 8);
+                if (a.bits) a.bits[b] = static_cast<uint8_t>(key);
             }
             logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz);
             softmax70(v);
@@ -386,6 +413,7 @@ __global__ __launch_bounds__(kWave) void bwd48_kernel(BwdArgs a) {
         const int64_t b = b0 + lane;
         tile_copy_in(SAVED ? a.y : a.z, b0, nb, tl);
         if (ACC) tile_copy_in(a.dz, b0, nb, reinterpret_cast<float *>(prev4));
+        lds_fill_wait();
         __syncthreads();
         float *row = tl + lane * kK;
         if (lane < nb) {
@@ -447,6 +475,7 @@ __global__ __launch_bounds__(kWave) void reg48_saved_kernel(RegArgs a) {
         const int64_t b0 = tile * kWave;
         const int nb = static_cast<int>(a.g.nblocks - b0 < kWave ? a.g.nblocks - b0 : kWave);
         tile_copy_in(a.y, b0, nb, reinterpret_cast<float *>(tile4));
+        lds_fill_wait();
         __syncthreads();
         if (lane < nb) {
             float m[8], w[8];
@@ -476,27 +505,12 @@ __global__ __launch_bounds__(kWave) void hard48_kernel(HardArgs a) {
         const int64_t b0 = tile * kWave;
         const int nb = static_cast<int>(a.g.nblocks - b0 < kWave ? a.g.nblocks - b0 : kWave);
         tile_copy_in(a.z, b0, nb, reinterpret_cast<float *>(tile4));
+        lds_fill_wait();
         __syncthreads();
         if (lane < nb) {
-            const float *row = tl + lane * kK;
-            int best = 0;
-            float bv = row[0];
-#pragma unroll
-            for (int i = 1; i < kK; ++i) {
-                const float x = row[i];
-                if (x > bv) {
-                    bv = x;
-                    best = i;
-                }
-            }
-            if (a.idx) a.idx[b0 + lane] = static_cast<uint8_t>(best);
-            if (a.bits) {
-                uint32_t mask = C48::at(0);
-#pragma unroll
-                for (int i = 1; i < kK; ++i)
-                    if (best == i) mask = C48::at(i);
-                a.bits[b0 + lane] = static_cast<uint8_t>(mask);
-            }
+            const uint32_t key = argmax_key70(tl + lane * kK);
+            if (a.idx) a.idx[b0 + lane] = static_cast<uint8_t>(key >> 8);
+            if (a.bits) a.bits[b0 + lane] = static_cast<uint8_t>(key);
         }
         __syncthreads();
     }
@@ -527,6 +541,7 @@ __global__ __launch_bounds__(kWave) void prior48_kernel(PriorArgs a) {
         const int nb = static_cast<int>(a.g.nblocks - b0 < kWave ? a.g.nblocks - b0 : kWave);
         const int64_t b = b0 + lane;
         tile_copy_in(a.z, b0, nb, tl);
+        lds_fill_wait();
         __syncthreads();
         if (lane < nb) {
             float *row = tl + lane * kK;
@@ -589,10 +604,18 @@ hipError_t go(Kern kernel, const A &args, int64_t nblocks, hipStream_t s) {
 
 hipError_t launch_fwd48(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype out_dt, hipStream_t s) {
     const int64_t n = a.g.nblocks;
-    if (w_dt == MASKGS_BF16 && out_dt == MASKGS_BF16) return go(fwd48_kernel<bf16_t, bf16_t>, a, n, s);
-    if (w_dt == MASKGS_BF16) return go(fwd48_kernel<bf16_t, float>, a, n, s);
-    if (out_dt == MASKGS_BF16) return go(fwd48_kernel<float, bf16_t>, a, n, s);
-    return go(fwd48_kernel<float, float>, a, n, s);
+    if (a.idx || a.bits) {
+        if (w_dt == MASKGS_BF16 && out_dt == MASKGS_BF16)
+            return go(fwd48_kernel<bf16_t, bf16_t, true>, a, n, s);
+        if (w_dt == MASKGS_BF16) return go(fwd48_kernel<bf16_t, float, true>, a, n, s);
+        if (out_dt == MASKGS_BF16) return go(fwd48_kernel<float, bf16_t, true>, a, n, s);
+        return go(fwd48_kernel<float, float, true>, a, n, s);
+    }
+    if (w_dt == MASKGS_BF16 && out_dt == MASKGS_BF16)
+        return go(fwd48_kernel<bf16_t, bf16_t, false>, a, n, s);
+    if (w_dt == MASKGS_BF16) return go(fwd48_kernel<bf16_t, float, false>, a, n, s);
+    if (out_dt == MASKGS_BF16) return go(fwd48_kernel<float, bf16_t, false>, a, n, s);
+    return go(fwd48_kernel<float, float, false>, a, n, s);
 }
 
 template <bool SAVED, bool ACC>
