@@ -45,6 +45,13 @@ __device__ __forceinline__ int half_count(int nb, int h) {
     return c < 0 ? 0 : (c > kHalf ? kHalf : c);
 }
 
+// LDS address of a generic pointer into a __shared__ array: the low 32 bits of
+// a generic pointer into the LDS aperture are the LDS byte offset.
+__device__ __forceinline__ __attribute__((address_space(3))) void *lds_addr(const void *p) {
+    return (__attribute__((address_space(3))) void *)static_cast<uintptr_t>(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
+}
+
 // Copies nf floats (16-byte aligned at both ends) from global memory into LDS
 // with direct-to-LDS loads (global_load_lds_dwordx4): lane l of round k moves
 // float4 number 64k+l, so every load of the tile is in flight at once and no
@@ -56,9 +63,8 @@ __device__ __forceinline__ void lds_fill(const float *src, float *lds, int nf) {
     for (int k = 0; k * kWave < n4; ++k) {
         const int i = k * kWave + lane;
         if (i < n4)
-            __builtin_amdgcn_global_load_lds(
-                reinterpret_cast<const float4 *>(src) + i,
-                (__attribute__((address_space(3))) void *)(lds + 4 * k * kWave), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const float4 *>(src) + i,
+                                             lds_addr(lds + 4 * k * kWave), 16, 0, 0);
     }
     if ((nf & 3) && lane == 0)
         reinterpret_cast<float2 *>(lds)[2 * n4] = reinterpret_cast<const float2 *>(src)[2 * n4];
@@ -67,6 +73,40 @@ __device__ __forceinline__ void lds_fill(const float *src, float *lds, int nf) {
 // Waits for this wave's outstanding memory operations, the direct-to-LDS
 // loads of lds_fill among them.
 __device__ __forceinline__ void lds_fill_wait() { __builtin_amdgcn_s_waitcnt(0); }
+
+// A tile's worth of floats held in registers between an LDS read and the
+// global stores: lane l keeps float4 numbers 64k+l (and lane 0 the odd float
+// pair at the end).  CAP is the float4 size of the LDS buffer.
+template <int CAP>
+struct TileRegs {
+    static constexpr int kRounds = (CAP + kWave - 1) / kWave;
+    float4 v[kRounds];
+    float2 tail;
+
+    // Reads the LDS buffer.  Every lane reads (a clamped, in-bounds index), so
+    // the array stays in registers; only the stores below are predicated.
+    __device__ __forceinline__ void gather(const float *lds, int nf) {
+        const int lane = threadIdx.x;
+#pragma unroll
+        for (int k = 0; k < kRounds; ++k) {
+            const int i = k * kWave + lane;
+            v[k] = reinterpret_cast<const float4 *>(lds)[i < CAP ? i : CAP - 1];
+        }
+        const int n4 = nf >> 2;
+        tail = reinterpret_cast<const float2 *>(lds)[(nf & 3) ? 2 * n4 : 0];
+    }
+    // Writes nf floats to dst (16-byte aligned).
+    __device__ __forceinline__ void scatter(float *dst, int nf) const {
+        const int lane = threadIdx.x;
+        const int n4 = nf >> 2;
+#pragma unroll
+        for (int k = 0; k < kRounds; ++k) {
+            const int i = k * kWave + lane;
+            if (i < n4) reinterpret_cast<float4 *>(dst)[i] = v[k];
+        }
+        if ((nf & 3) && lane == 0) reinterpret_cast<float2 *>(dst)[2 * n4] = tail;
+    }
+};
 
 template <bool ADD>
 __device__ __forceinline__ void tile_in(const float *g, int64_t b0, int nb, float *stage,
@@ -127,13 +167,9 @@ __device__ __forceinline__ void tile_copy_in(const float *g, int64_t b0, int nb,
 }
 
 __device__ __forceinline__ void tile_copy_out(float *g, int64_t b0, int nb, const float *lds) {
-    const int lane = threadIdx.x;
-    float *dst = g + b0 * kK;
-    const int nf = nb * kK, n4 = nf >> 2;
-    for (int i = lane; i < n4; i += kWave)
-        reinterpret_cast<float4 *>(dst)[i] = reinterpret_cast<const float4 *>(lds)[i];
-    if ((nf & 3) && lane == 0)
-        reinterpret_cast<float2 *>(dst)[2 * n4] = reinterpret_cast<const float2 *>(lds)[2 * n4];
+    TileRegs<kWave * kK / 4> r;
+    r.gather(lds, nb * kK);
+    r.scatter(g + b0 * kK, nb * kK);
 }
 
 // 8 weights / gradients of one block.
@@ -375,22 +411,42 @@ __global__ __launch_bounds__(kWave) void reg48_noise_kernel(RegArgs a) {
 // in each pass instead of being kept in registers across passes.
 __device__ __forceinline__ void row_pass_barrier() { asm volatile("" ::: "memory"); }
 
-// Soft mask of a row in fp32 and fp64 (Eq. 7).
-__device__ __forceinline__ void row_soft_mask(const float *row, float (&m)[8], double (&md)[8]) {
+// Soft mask of a row in fp32 (Eq. 7), candidates in table order.
+__device__ __forceinline__ void row_soft_mask(const float *row, float (&m)[8]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        m[j] = 0.0f;
-        md[j] = 0.0;
-    }
+    for (int j = 0; j < 8; ++j) m[j] = 0.0f;
 #pragma unroll
     for (int i = 0; i < kK; ++i) {
         const float y = row[i];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            if ((C48::at(i) >> j) & 1u) {
-                m[j] += y;
-                md[j] += static_cast<double>(y);
-            }
+            if ((C48::at(i) >> j) & 1u) m[j] += y;
+    }
+}
+
+// Kept positions of every candidate, ascending: kPos.p[i][k] is the k-th set
+// bit of S_i.  A compile-time table, so unrolled uses fold to constants.
+struct PosTable {
+    uint8_t p[kK][4];
+    constexpr PosTable() : p() {
+        for (int i = 0; i < kK; ++i) {
+            int k = 0;
+            for (int j = 0; j < 8; ++j)
+                if ((C48::at(i) >> j) & 1u) p[i][k++] = static_cast<uint8_t>(j);
+        }
+    }
+};
+constexpr PosTable kPos{};
+
+// Soft mask of a row, summed in fp64 (Eq. 7).
+__device__ __forceinline__ void row_soft_mask_f64(const float *row, double (&md)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) md[j] = 0.0;
+#pragma unroll
+    for (int i = 0; i < kK; ++i) {
+        const double y = static_cast<double>(row[i]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) md[kPos.p[i][k]] += y;
     }
 }
 
@@ -413,6 +469,13 @@ __global__ __launch_bounds__(kWave) void bwd48_kernel(BwdArgs a) {
         const int64_t b = b0 + lane;
         tile_copy_in(SAVED ? a.y : a.z, b0, nb, tl);
         if (ACC) tile_copy_in(a.dz, b0, nb, reinterpret_cast<float *>(prev4));
+        // the block's weights and upstream gradient are requested with the tile,
+        // so one wait covers all of them
+        float w[8], G[8];
+        if (lane < nb) {
+            Io8<WT>::load(a.w, b, w);
+            Io8<GT>::load(a.dout, b, G);
+        }
         lds_fill_wait();
         __syncthreads();
         float *row = tl + lane * kK;
@@ -427,11 +490,11 @@ __global__ __launch_bounds__(kWave) void bwd48_kernel(BwdArgs a) {
                 for (int i = 0; i < kK; ++i) row[i] = v[i];
                 row_pass_barrier();
             }
-            float m[8], w[8], G[8];
+            float m[8];
             double md[8], dm[8];
-            row_soft_mask(row, m, md);
-            Io8<WT>::load(a.w, b, w);
-            Io8<GT>::load(a.dout, b, G);
+            row_soft_mask_f64(row, md);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m[j] = static_cast<float>(md[j]);
             // s = sum_i y_i dy_i / sum_i y_i = sum_j m_j dm_j / (sum_j m_j / 4): the
             // division by the actual sum of the fp32 soft index keeps dy_i - s
             // free of the fp32 rounding of y (see the 2:4 backward)
@@ -444,17 +507,30 @@ __global__ __launch_bounds__(kWave) void bwd48_kernel(BwdArgs a) {
                 msum += md[j];
             }
             s = s * 4.0 / msum;
+            // dy_i = (dm_a + dm_b) + (dm_c + dm_d) for S_i = {a < b < c < d}:
+            // two of the 28 pair sums per candidate
+            double pair[8][8];
+#pragma unroll
+            for (int p = 0; p < 8; ++p)
+#pragma unroll
+                for (int q = p + 1; q < 8; ++q) pair[p][q] = dm[p] + dm[q];
             row_pass_barrier();
             const float *prow = pv + lane * kK;
+            const float scale32 = static_cast<float>(a.nz.grad_scale);
 #pragma unroll
             for (int i = 0; i < kK; ++i) {
-                double dy = 0.0;
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if ((C48::at(i) >> j) & 1u) dy += dm[j];
-                double d = a.nz.grad_scale * static_cast<double>(row[i]) * (dy - s);
-                if (ACC) d += static_cast<double>(prow[i]);
-                row[i] = static_cast<float>(d);
+                const int p0 = kPos.p[i][0], p1 = kPos.p[i][1];
+                const int p2 = kPos.p[i][2], p3 = kPos.p[i][3];
+                const double dys = (pair[p0][p1] + pair[p2][p3]) - s;
+                if (ACC) {
+                    const double d = a.nz.grad_scale * static_cast<double>(row[i]) * dys +
+                                     static_cast<double>(prow[i]);
+                    row[i] = static_cast<float>(d);
+                } else {
+                    // the cancellation dy_i - s is taken in fp64; the scaling by
+                    // (kappa/tau) y_i adds three fp32 roundings (< 3e-7 relative)
+                    row[i] = (scale32 * row[i]) * static_cast<float>(dys);
+                }
             }
         }
         __syncthreads();
@@ -479,8 +555,7 @@ __global__ __launch_bounds__(kWave) void reg48_saved_kernel(RegArgs a) {
         __syncthreads();
         if (lane < nb) {
             float m[8], w[8];
-            double md[8];
-            row_soft_mask(tl + lane * kK, m, md);
+            row_soft_mask(tl + lane * kK, m);
             Io8<WT>::load(a.w, b0 + lane, w);
             float racc = 0.0f;
 #pragma unroll
