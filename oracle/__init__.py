@@ -78,6 +78,9 @@ def lib():
     L.orc_hard_extract.argtypes = [c.c_int, c.c_int, c.c_int64, c.c_int64, P, P, c.c_int,
                                    P, P, P, P]
     L.orc_hard_extract.restype = c.c_int
+    L.orc_adamw.argtypes = [c.c_int64, P, P, P, P, c.c_double, c.c_double, c.c_double,
+                            c.c_double, c.c_double, c.c_uint32]
+    L.orc_adamw.restype = c.c_int
     L.orc_magnitude_mask.argtypes = [c.c_int, c.c_int, c.c_int64, c.c_int64, P, P]
     L.orc_magnitude_mask.restype = c.c_int
     L.orc_prior_init.argtypes = [c.c_int, c.c_int, c.c_int64, c.c_int64, P, P, P,
@@ -202,6 +205,21 @@ def bwd(n, m, w, z, g_up, *, kappa, tau, lam, seed=0, step=0, tensor_id=0, block
     if rc != 0:
         raise ValueError("oracle bwd: invalid arguments")
     return dz
+
+
+def adamw(z, g, m, v, *, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1, t=1):
+    """One AdamW update of the logits z with gradient g (fp32 arrays of one
+    shape); returns new (z, m, v) as fp32 arrays, inputs untouched.  The
+    update rule and its reading are in maskgs_oracle.c (orc_adamw)."""
+    z = _f32(z).copy()
+    g = _f32(g).reshape(z.shape)
+    m = _f32(m).reshape(z.shape).copy()
+    v = _f32(v).reshape(z.shape).copy()
+    rc = lib().orc_adamw(z.size, _ptr(z), _ptr(g), _ptr(m), _ptr(v), float(lr), float(beta1),
+                         float(beta2), float(eps), float(weight_decay), int(t))
+    if rc != 0:
+        raise ValueError("oracle adamw: invalid arguments")
+    return z, m, v
 
 
 def hard_extract(n, m, z, rows, cols, w_raw=None):

@@ -512,3 +512,39 @@ int orc_prior_init(int n, int m, int64_t rows, int64_t cols, float *z, const uin
     free(own);
     return 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* AdamW update of the logits (MaskLLM summary, section 3.4, Algorithm 1     */
+/* "update logits", and the training details: AdamW with lr 5e-4 for LLaMA-2 */
+/* and Nemotron, weight decay 0.1).  The pages fix neither the moment        */
+/* coefficients, nor epsilon, nor how the decay enters; the reading here is  */
+/* Adam (Kingma & Ba, ICLR 2015: moments, bias correction) with decoupled    */
+/* weight decay (Loshchilov & Hutter, ICLR 2019) scaled by the learning rate:*/
+/*   m  = b1 m + (1 - b1) g            v  = b2 v + (1 - b2) g^2              */
+/*   mh = m / (1 - b1^t)               vh = v / (1 - b2^t)                   */
+/*   z  = z - lr (mh / (sqrt(vh) + eps) + wd z)    (z on the right: before   */
+/*                                                  this step)               */
+/* t >= 1 is the number of updates including this one.  Every operation in   */
+/* fp64 from the fp32 inputs; z, m and v are rounded to fp32 once.  g is the */
+/* logit gradient as stored (fp32).                                          */
+/* ------------------------------------------------------------------------- */
+int orc_adamw(int64_t count, float *z, const float *g, float *m, float *v, double lr,
+              double b1, double b2, double eps, double wd, uint32_t t) {
+    if (count < 0 || t < 1) return -1;
+    double bc1 = 1.0 - pow(b1, (double)t);
+    double bc2 = 1.0 - pow(b2, (double)t);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        double gi = (double)g[i];
+        double mi = b1 * (double)m[i] + (1.0 - b1) * gi;
+        double vi = b2 * (double)v[i] + (1.0 - b2) * gi * gi;
+        double mh = mi / bc1;
+        double vh = vi / bc2;
+        double zi = (double)z[i];
+        double zn = zi - lr * (mh / (sqrt(vh) + eps) + wd * zi);
+        z[i] = (float)zn;
+        m[i] = (float)mi;
+        v[i] = (float)vi;
+    }
+    return 0;
+}

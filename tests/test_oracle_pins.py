@@ -556,3 +556,74 @@ def test_steps_and_tensors_draw_fresh_noise(orc):
     assert not np.allclose(ys[0], ys[1]) and not np.allclose(ys[0], ys[2])
     again = orc.fwd(2, 4, w, z, kappa=100.0, tau=4.0, step=1, tensor_id=0)["y"]
     assert np.array_equal(again, ys[1])
+
+
+# --------------------------------------------------------------------------
+# AdamW on the logits (section 3.4, Algorithm 1 "update logits"; training
+# details: AdamW, lr 5e-4 for LLaMA-2 / Nemotron, weight decay 0.1)
+# --------------------------------------------------------------------------
+def _adamw_state(n, seed):
+    rng = np.random.default_rng(seed)
+    z = rng.normal(0, 1, n).astype(np.float32)
+    g = (rng.normal(0, 1e-4, n) * rng.choice([1e-3, 1.0, 30.0], n)).astype(np.float32)
+    g[:7] = 0.0
+    m = rng.normal(0, 1e-4, n).astype(np.float32)
+    v = (rng.normal(0, 1e-4, n) ** 2).astype(np.float32)
+    return z, g, m, v
+
+
+@pytest.mark.parametrize("t", [1, 2, 7, 100, 2000])
+def test_adamw_matches_torch_reference(orc, t):
+    """Independent implementation: torch.optim.AdamW in fp64 on the CPU, with
+    the oracle's fp32 state injected; the oracle is its fp32 rounding."""
+    import torch
+    z, g, m, v = _adamw_state(4096, t)
+    if t == 1:
+        m[:] = 0.0
+        v[:] = 0.0
+    hp = dict(lr=5e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1)
+    zo, mo, vo = orc.adamw(z, g, m, v, t=t, **hp)
+    p = torch.nn.Parameter(torch.from_numpy(z.astype(np.float64)))
+    opt = torch.optim.AdamW([p], lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                            weight_decay=hp["weight_decay"], foreach=False)
+    if t > 1:
+        opt.state[p] = {"step": torch.tensor(float(t - 1), dtype=torch.float64),
+                        "exp_avg": torch.from_numpy(m.astype(np.float64)),
+                        "exp_avg_sq": torch.from_numpy(v.astype(np.float64))}
+    p.grad = torch.from_numpy(g.astype(np.float64))
+    opt.step()
+    st = opt.state[p]
+    for got, ref, what in [(zo, p.detach().numpy(), "z"), (mo, st["exp_avg"].numpy(), "m"),
+                           (vo, st["exp_avg_sq"].numpy(), "v")]:
+        # fp32 rounding of the fp64 result (plus a few fp64 ulps)
+        bound = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64) * 0.5 + 1e-15 * np.abs(ref)
+        assert (np.abs(got.astype(np.float64) - ref) <= bound + 1e-45).all(), (what, t)
+
+
+def test_adamw_first_step_closed_form(orc):
+    """From zero moments, the first bias-corrected step is g/(|g| + eps) per
+    logit: z1 = z0 - lr (g/(|g|+eps) + wd z0)."""
+    z, g, _, _ = _adamw_state(2048, 5)
+    zero = np.zeros_like(z)
+    lr, wd, eps = 5e-4, 0.1, 1e-8
+    zo, mo, vo = orc.adamw(z, g, zero, zero, lr=lr, eps=eps, weight_decay=wd, t=1)
+    z64, g64 = z.astype(np.float64), g.astype(np.float64)
+    ref = z64 - lr * (g64 / (np.abs(g64) + eps) + wd * z64)
+    assert np.array_equal(zo, ref.astype(np.float32))
+    assert np.array_equal(mo, (0.1 * g64).astype(np.float32))
+    assert np.array_equal(vo, (0.001 * g64 * g64).astype(np.float32))
+
+
+def test_adamw_degenerate_cases(orc):
+    z, g, m, v = _adamw_state(1024, 9)
+    # lr = 0: the logits do not move, the moments still advance
+    zo, mo, vo = orc.adamw(z, g, m, v, lr=0.0, t=3)
+    assert np.array_equal(zo, z)
+    assert not np.array_equal(mo, m)
+    # no gradient, no decay, zero moments: nothing moves
+    zero = np.zeros_like(z)
+    zo, mo, vo = orc.adamw(z, zero, zero, zero, lr=5e-4, weight_decay=0.0, t=4)
+    assert np.array_equal(zo, z) and not mo.any() and not vo.any()
+    # decay alone shrinks z by the factor (1 - lr wd)
+    zo, _, _ = orc.adamw(z, zero, zero, zero, lr=5e-4, weight_decay=0.1, t=4)
+    assert np.array_equal(zo, (z.astype(np.float64) * (1 - 5e-5)).astype(np.float32))
