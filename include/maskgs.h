@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MASKGS_ABI_VERSION 1
+#define MASKGS_ABI_VERSION 2
 
 /* Status codes. */
 #define MASKGS_OK 0
@@ -143,6 +143,42 @@ int maskgs_bwd(const maskgs_tensor_desc *t, const maskgs_sample_params *p, const
                maskgs_dtype w_dt, const float *z, const float *y_saved, const void *dout,
                maskgs_dtype dout_dt, float lambda, float *dz, int32_t accumulate,
                hipStream_t stream);
+
+/* AdamW hyperparameters of maskgs_bwd_adamw (section 3.4, Algorithm 1 "update
+ * logits", and the training details: AdamW, lr 5e-4 for LLaMA-2 and Nemotron,
+ * 1e-3 for GPT-3, weight decay 0.1).  The pages give no beta1, beta2 or eps;
+ * Adam's published defaults are 0.9, 0.999 and 1e-8.  The weight decay is
+ * decoupled from the moments and scaled by lr. */
+typedef struct {
+    float lr;           /* >= 0                                              */
+    float beta1, beta2; /* in [0, 1)                                         */
+    float eps;          /* > 0                                               */
+    float weight_decay; /* >= 0                                              */
+    uint32_t t;         /* updates so far including this one (>= 1), for the */
+                        /* bias corrections 1 - beta^t                       */
+} maskgs_adamw_params;
+
+/* Backward to the logits fused with their AdamW update (section 3.4,
+ * Algorithm 1: backpropagate, then update the logits).  dz is computed exactly
+ * as maskgs_bwd with accumulate = 0 stores it (fp32) but is never written;
+ * instead, per logit,
+ *   m = b1 m + (1 - b1) dz,   v = b2 v + (1 - b2) dz^2,
+ *   z = z - lr (m / (1 - b1^t) / (sqrt(v / (1 - b2^t)) + eps) + wd z),
+ * with z on the right the logits before this update.
+ *   z          [B, K] fp32, in-out: read for the soft index when y_saved is
+ *              NULL and for the update, then overwritten with the new logits.
+ *   y_saved    NULL (recompute y from z before the update, bit-identical to the
+ *              forward's) or the y_save of maskgs_fwd.
+ *   exp_avg, exp_avg_sq  [B, K] fp32 first and second moments, in-out (zero
+ *              before the first update).
+ *   opt        HOST pointer to the hyperparameters.
+ * Other arguments as in maskgs_bwd.  E_RANGE for lr < 0, beta outside [0, 1),
+ * eps <= 0, weight_decay < 0, t = 0 or a non-finite value.  z, exp_avg and
+ * exp_avg_sq must not alias each other or any input. */
+int maskgs_bwd_adamw(const maskgs_tensor_desc *t, const maskgs_sample_params *p, const void *w,
+                     maskgs_dtype w_dt, float *z, const float *y_saved, const void *dout,
+                     maskgs_dtype dout_dt, float lambda, float *exp_avg, float *exp_avg_sq,
+                     const maskgs_adamw_params *opt, hipStream_t stream);
 
 /* Regulariser value alone (section 3.4, Eq. 8): adds sum_b ||W_b (.) M~_b||^2 to
  * *reg_accum (one device double, atomically) without writing W (.) M~.

@@ -35,7 +35,7 @@ MASKGS_NO_NOISE = 1
 
 EXPORTS = ("maskgs_abi_version", "maskgs_status_str", "maskgs_candidates", "maskgs_fwd",
            "maskgs_fwd_hard",
-           "maskgs_bwd", "maskgs_reg_reduce", "maskgs_hard_extract", "maskgs_prior_init",
+           "maskgs_bwd", "maskgs_bwd_adamw", "maskgs_reg_reduce", "maskgs_hard_extract", "maskgs_prior_init",
            "maskgs_debug_philox", "maskgs_debug_gumbel")
 
 
@@ -56,6 +56,12 @@ class SampleParams(ctypes.Structure):
     """maskgs_sample_params: Philox seed and step, kappa, tau, flags."""
     _fields_ = [("seed", ctypes.c_uint64), ("step", ctypes.c_uint32), ("kappa", ctypes.c_float),
                 ("tau", ctypes.c_float), ("flags", ctypes.c_uint32)]
+
+
+class AdamWParams(ctypes.Structure):
+    """maskgs_adamw_params: lr, beta1, beta2, eps, weight decay, update count t."""
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("t", ctypes.c_uint32)]
 
 
 _lib = None
@@ -81,6 +87,8 @@ def load_library(path: str = LIB_PATH):
     L.maskgs_fwd.argtypes = [DP, SP, P, c.c_int, P, P, c.c_int, P, P, P]
     L.maskgs_fwd_hard.argtypes = [DP, SP, P, c.c_int, P, P, c.c_int, P, P, P, P, P, P, P]
     L.maskgs_bwd.argtypes = [DP, SP, P, c.c_int, P, P, P, c.c_int, c.c_float, P, c.c_int32, P]
+    L.maskgs_bwd_adamw.argtypes = [DP, SP, P, c.c_int, P, P, P, c.c_int, c.c_float, P, P,
+                                   c.POINTER(AdamWParams), P]
     L.maskgs_reg_reduce.argtypes = [DP, SP, P, c.c_int, P, P, P, P]
     L.maskgs_hard_extract.argtypes = [DP, P, P, c.c_int, P, P, P, P, P]
     L.maskgs_prior_init.argtypes = [DP, P, P, P, c.c_int, c.c_float, c.c_int32, P]
@@ -232,6 +240,28 @@ def maskgs_bwd(t: Tensor, p: SampleParams, w, z, y_saved, dout, lam: float, dz,
         float(lam), _ptr(dz, "dz", f32, t.nblocks * t.k, dev), int(bool(accumulate)),
         _stream(stream)))
     return dz
+
+
+def maskgs_bwd_adamw(t: Tensor, p: SampleParams, w, z, y_saved, dout, lam: float, exp_avg,
+                     exp_avg_sq, lr: float, beta1: float = 0.9, beta2: float = 0.999,
+                     eps: float = 1e-8, weight_decay: float = 0.1, step_t: int = 1,
+                     stream=None):
+    """Backward to the logits fused with their AdamW update (section 3.4,
+    Algorithm 1): z, exp_avg and exp_avg_sq are updated in place."""
+    dev = w.device
+    f32 = _torch().float32
+    opt = AdamWParams(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
+                      int(step_t))
+    _check("maskgs_bwd_adamw", load_library().maskgs_bwd_adamw(
+        ctypes.byref(t.desc()), ctypes.byref(p),
+        _ptr(w, "w", numel=t.rows * t.cols, device=dev), _dtype_code(w),
+        _ptr(z, "z", f32, t.nblocks * t.k, dev),
+        _ptr(y_saved, "y_saved", f32, t.nblocks * t.k, dev),
+        _ptr(dout, "dout", numel=t.rows * t.cols, device=dev), _dtype_code(dout),
+        float(lam), _ptr(exp_avg, "exp_avg", f32, t.nblocks * t.k, dev),
+        _ptr(exp_avg_sq, "exp_avg_sq", f32, t.nblocks * t.k, dev), ctypes.byref(opt),
+        _stream(stream)))
+    return z
 
 
 def maskgs_reg_reduce(t: Tensor, p: SampleParams, w, z, y_saved, reg_accum, stream=None):

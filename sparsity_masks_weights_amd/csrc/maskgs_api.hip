@@ -176,6 +176,49 @@ int maskgs_bwd(const maskgs_tensor_desc *t, const maskgs_sample_params *p, const
     return launch_status(launch_bwd48(a, w_dt, dout_dt, stream));
 }
 
+int maskgs_bwd_adamw(const maskgs_tensor_desc *t, const maskgs_sample_params *p, const void *w,
+                     maskgs_dtype w_dt, float *z, const float *y_saved, const void *dout,
+                     maskgs_dtype dout_dt, float lambda, float *exp_avg, float *exp_avg_sq,
+                     const maskgs_adamw_params *opt, hipStream_t stream) {
+    Geometry g;
+    Noise nz;
+    int rc = check_desc(t, &g);
+    if (rc) return rc;
+    if ((rc = check_params(p, &nz))) return rc;
+    if (!opt) return MASKGS_E_NULL;
+    if (!std::isfinite(lambda) || lambda < 0.0f) return MASKGS_E_RANGE;
+    const float vals[5] = {opt->lr, opt->beta1, opt->beta2, opt->eps, opt->weight_decay};
+    for (float v : vals)
+        if (!std::isfinite(v)) return MASKGS_E_RANGE;
+    if (opt->lr < 0.0f || !(opt->beta1 >= 0.0f && opt->beta1 < 1.0f) ||
+        !(opt->beta2 >= 0.0f && opt->beta2 < 1.0f) || !(opt->eps > 0.0f) ||
+        opt->weight_decay < 0.0f || opt->t == 0)
+        return MASKGS_E_RANGE;
+    if (g.nblocks == 0) return MASKGS_OK;
+    if (!w || !dout || !z || !exp_avg || !exp_avg_sq) return MASKGS_E_NULL;
+    if (!valid_dtype(w_dt) || !valid_dtype(dout_dt)) return MASKGS_E_DTYPE;
+    if (misaligned(w) || misaligned(z) || misaligned(y_saved) || misaligned(dout) ||
+        misaligned(exp_avg) || misaligned(exp_avg_sq))
+        return MASKGS_E_ALIGN;
+    BwdArgs a{w, z, y_saved, dout, nullptr, static_cast<double>(lambda), false, g, nz};
+    a.zu = z;
+    a.m1 = exp_avg;
+    a.m2 = exp_avg_sq;
+    const double t_d = static_cast<double>(opt->t);
+    a.adam.lr = opt->lr;
+    a.adam.b1 = opt->beta1;
+    a.adam.omb1 = static_cast<float>(1.0 - static_cast<double>(opt->beta1));
+    a.adam.b2 = opt->beta2;
+    a.adam.omb2 = static_cast<float>(1.0 - static_cast<double>(opt->beta2));
+    a.adam.ibc1 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(opt->beta1), t_d)));
+    a.adam.ibc2 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(opt->beta2), t_d)));
+    a.adam.eps = opt->eps;
+    a.adam.wd = opt->weight_decay;
+    if (!std::isfinite(a.adam.ibc1) || !std::isfinite(a.adam.ibc2)) return MASKGS_E_RANGE;
+    if (g.m == 4) return launch_status(launch_bwd24(a, w_dt, dout_dt, stream));
+    return launch_status(launch_bwd48(a, w_dt, dout_dt, stream));
+}
+
 int maskgs_reg_reduce(const maskgs_tensor_desc *t, const maskgs_sample_params *p, const void *w,
                       maskgs_dtype w_dt, const float *z, const float *y_saved,
                       double *reg_accum, hipStream_t stream) {

@@ -173,12 +173,18 @@ __device__ __forceinline__ void nt_store(float4 *p, float4 v) {
 // Stores 12 floats per lane for the workgroup tile of pairs [base, base+256):
 // lanes stage their values in LDS, then the tile (contiguous in memory) is
 // written with coalesced 16 B stores.  Called by every lane of the workgroup.
-__device__ __forceinline__ void store12_tile(float *g, int64_t base, int64_t nblocks,
-                                             const float (&v)[12], float4 *lds) {
+// Writes a lane's 12 values to its slot of the LDS tile (pair order).
+__device__ __forceinline__ void stage12(const float (&v)[12], float4 *lds) {
     const int t = threadIdx.x;
     lds[3 * t] = make_float4(v[0], v[1], v[2], v[3]);
     lds[3 * t + 1] = make_float4(v[4], v[5], v[6], v[7]);
     lds[3 * t + 2] = make_float4(v[8], v[9], v[10], v[11]);
+}
+
+__device__ __forceinline__ void store12_tile(float *g, int64_t base, int64_t nblocks,
+                                             const float (&v)[12], float4 *lds) {
+    const int t = threadIdx.x;
+    stage12(v, lds);
     __syncthreads();
     const int64_t end = 2 * (base + kThreads) < nblocks ? 2 * (base + kThreads) : nblocks;
     const int nf = static_cast<int>((end - 2 * base) * 6);
@@ -384,7 +390,7 @@ __global__ __launch_bounds__(kThreads) void fwd24_kernel(FwdArgs a) {
 //   dm_j = G_j w_j - 2 lambda w_j (w_j m_j),  dy_i = sum_j S_ij dm_j,
 //   dz_i = (kappa/tau) y_i (dy_i - sum_k y_k dy_k)       (fp64 arithmetic)
 // ---------------------------------------------------------------------------
-template <int PHASE, typename WT, typename GT, bool SAVED>
+template <int PHASE, typename WT, typename GT, bool SAVED, bool ADAMW>
 __global__ __launch_bounds__(kThreads) void bwd24_kernel(BwdArgs a) {
     __shared__ float4 stage[3 * kThreads];
     const int64_t npairs = (a.g.nblocks + 1) >> 1;
@@ -443,7 +449,22 @@ __global__ __launch_bounds__(kThreads) void bwd24_kernel(BwdArgs a) {
                 }
             }
         }
-        store12_tile(a.dz, base, a.g.nblocks, dz, stage);
+        if (ADAMW) {
+            // the gradient tile goes through LDS into the AdamW update of the
+            // same logits (coalesced float4 streams of z and both moments)
+            stage12(dz, stage);
+            __syncthreads();
+            const int64_t end = 2 * (base + kThreads) < a.g.nblocks ? 2 * (base + kThreads)
+                                                                   : a.g.nblocks;
+            const int nf = static_cast<int>((end - 2 * base) * 6);
+            adamw_span<kThreads, 3 * kThreads, 3>(a.zu + base * 12, a.m1 + base * 12,
+                                                  a.m2 + base * 12,
+                                                  reinterpret_cast<const float *>(stage), nf,
+                                                  a.adam);
+            __syncthreads();
+        } else {
+            store12_tile(a.dz, base, a.g.nblocks, dz, stage);
+        }
     }
 }
 
@@ -611,17 +632,25 @@ hipError_t fwd24_dispatch(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype o_dt
     return go(fwd24_kernel<PHASE, float, float>, a, np, s);
 }
 
-template <int PHASE, bool SAVED>
-hipError_t bwd24_dispatch(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt,
-                          hipStream_t s) {
+template <int PHASE, bool SAVED, bool ADAMW>
+hipError_t bwd24_dispatch(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, hipStream_t s) {
     const int64_t np = (a.g.nblocks + 1) >> 1;
     if (w_dt == MASKGS_BF16 && g_dt == MASKGS_BF16)
-        return go(bwd24_kernel<PHASE, bf16_t, bf16_t, SAVED>, a, np, s);
-    if (w_dt == MASKGS_BF16 && g_dt == MASKGS_F32)
-        return go(bwd24_kernel<PHASE, bf16_t, float, SAVED>, a, np, s);
-    if (w_dt == MASKGS_F32 && g_dt == MASKGS_BF16)
-        return go(bwd24_kernel<PHASE, float, bf16_t, SAVED>, a, np, s);
-    return go(bwd24_kernel<PHASE, float, float, SAVED>, a, np, s);
+        return go(bwd24_kernel<PHASE, bf16_t, bf16_t, SAVED, ADAMW>, a, np, s);
+    if (w_dt == MASKGS_BF16)
+        return go(bwd24_kernel<PHASE, bf16_t, float, SAVED, ADAMW>, a, np, s);
+    if (g_dt == MASKGS_BF16)
+        return go(bwd24_kernel<PHASE, float, bf16_t, SAVED, ADAMW>, a, np, s);
+    return go(bwd24_kernel<PHASE, float, float, SAVED, ADAMW>, a, np, s);
+}
+
+template <bool ADAMW>
+hipError_t bwd24_phase(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, hipStream_t s) {
+    const bool even = phase_of(a.g.block_offset) == 0;
+    if (a.y) return even ? bwd24_dispatch<0, true, ADAMW>(a, w_dt, g_dt, s)
+                         : bwd24_dispatch<2, true, ADAMW>(a, w_dt, g_dt, s);
+    return even ? bwd24_dispatch<0, false, ADAMW>(a, w_dt, g_dt, s)
+                : bwd24_dispatch<2, false, ADAMW>(a, w_dt, g_dt, s);
 }
 
 template <int PHASE, bool SAVED>
@@ -639,11 +668,7 @@ hipError_t launch_fwd24(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype out_dt
 }
 
 hipError_t launch_bwd24(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, hipStream_t s) {
-    const bool even = phase_of(a.g.block_offset) == 0;
-    if (a.y) return even ? bwd24_dispatch<0, true>(a, w_dt, g_dt, s)
-                         : bwd24_dispatch<2, true>(a, w_dt, g_dt, s);
-    return even ? bwd24_dispatch<0, false>(a, w_dt, g_dt, s)
-                : bwd24_dispatch<2, false>(a, w_dt, g_dt, s);
+    return a.m1 ? bwd24_phase<true>(a, w_dt, g_dt, s) : bwd24_phase<false>(a, w_dt, g_dt, s);
 }
 
 hipError_t launch_reg24(const RegArgs &a, maskgs_dtype w_dt, hipStream_t s) {

@@ -454,7 +454,7 @@ __device__ __forceinline__ void row_soft_mask_f64(const float *row, double (&md)
 // dm_j = G_j w_j - 2 lambda w_j (w_j m_j); sum_i y_i dy_i = sum_j m_j dm_j;
 // dz_i = (kappa/tau) y_i (dy_i - s), dy_i = sum_{j in S_i} dm_j, with
 // s = sum_i y_i dy_i / sum_i y_i.
-template <typename WT, typename GT, bool SAVED, bool ACC>
+template <typename WT, typename GT, bool SAVED, bool ACC, bool ADAMW>
 __global__ __launch_bounds__(kWave) void bwd48_kernel(BwdArgs a) {
     __shared__ float4 tile4[kWave * kK / 4];
     __shared__ float4 prev4[ACC ? kWave * kK / 4 : 1];
@@ -534,7 +534,13 @@ __global__ __launch_bounds__(kWave) void bwd48_kernel(BwdArgs a) {
             }
         }
         __syncthreads();
-        tile_copy_out(a.dz, b0, nb, tl);
+        if (ADAMW) {
+            // the gradient tile in LDS feeds the AdamW update of the same logits
+            adamw_span<kWave, kWave * kK / 4, 6>(a.zu + b0 * kK, a.m1 + b0 * kK, a.m2 + b0 * kK,
+                                                 tl, nb * kK, a.adam);
+        } else {
+            tile_copy_out(a.dz, b0, nb, tl);
+        }
         __syncthreads();
     }
 }
@@ -693,21 +699,24 @@ hipError_t launch_fwd48(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype out_dt
     return go(fwd48_kernel<float, float, false>, a, n, s);
 }
 
-template <bool SAVED, bool ACC>
+template <bool SAVED, bool ACC, bool ADAMW>
 hipError_t bwd48_dispatch(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, hipStream_t s) {
     const int64_t n = a.g.nblocks;
     const bool wb = w_dt == MASKGS_BF16, gb = g_dt == MASKGS_BF16;
-    if (wb && gb) return go(bwd48_kernel<bf16_t, bf16_t, SAVED, ACC>, a, n, s);
-    if (wb) return go(bwd48_kernel<bf16_t, float, SAVED, ACC>, a, n, s);
-    if (gb) return go(bwd48_kernel<float, bf16_t, SAVED, ACC>, a, n, s);
-    return go(bwd48_kernel<float, float, SAVED, ACC>, a, n, s);
+    if (wb && gb) return go(bwd48_kernel<bf16_t, bf16_t, SAVED, ACC, ADAMW>, a, n, s);
+    if (wb) return go(bwd48_kernel<bf16_t, float, SAVED, ACC, ADAMW>, a, n, s);
+    if (gb) return go(bwd48_kernel<float, bf16_t, SAVED, ACC, ADAMW>, a, n, s);
+    return go(bwd48_kernel<float, float, SAVED, ACC, ADAMW>, a, n, s);
 }
 
 hipError_t launch_bwd48(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, hipStream_t s) {
-    if (a.y) return a.accumulate ? bwd48_dispatch<true, true>(a, w_dt, g_dt, s)
-                                 : bwd48_dispatch<true, false>(a, w_dt, g_dt, s);
-    return a.accumulate ? bwd48_dispatch<false, true>(a, w_dt, g_dt, s)
-                        : bwd48_dispatch<false, false>(a, w_dt, g_dt, s);
+    if (a.m1)  // fused AdamW update (never with accumulation)
+        return a.y ? bwd48_dispatch<true, false, true>(a, w_dt, g_dt, s)
+                   : bwd48_dispatch<false, false, true>(a, w_dt, g_dt, s);
+    if (a.y) return a.accumulate ? bwd48_dispatch<true, true, false>(a, w_dt, g_dt, s)
+                                 : bwd48_dispatch<true, false, false>(a, w_dt, g_dt, s);
+    return a.accumulate ? bwd48_dispatch<false, true, false>(a, w_dt, g_dt, s)
+                        : bwd48_dispatch<false, false, false>(a, w_dt, g_dt, s);
 }
 
 hipError_t launch_reg48(const RegArgs &a, maskgs_dtype w_dt, hipStream_t s) {

@@ -42,16 +42,28 @@ struct FwdArgs {
     uint8_t *val_idx = nullptr;
 };
 
+// AdamW constants of one update, prepared on the host: 1 - beta and the
+// reciprocal bias corrections 1/(1 - beta^t) rounded to fp32.
+struct Adam {
+    float lr, b1, omb1, b2, omb2, ibc1, ibc2, eps, wd;
+};
+
 struct BwdArgs {
     const void *w;
     const float *z;  // nullable when y is given
     const float *y;  // nullable: recompute
     const void *dout;
-    float *dz;
+    float *dz;       // the logit gradient (nullptr under the fused AdamW update)
     double lambda;
     bool accumulate;
     Geometry g;
     Noise nz;
+    // fused AdamW update (maskgs_bwd_adamw): the logits updated in place (the
+    // same array as z) and the two moments; all nullptr otherwise
+    float *zu = nullptr;
+    float *m1 = nullptr;
+    float *m2 = nullptr;
+    Adam adam{};
 };
 
 struct RegArgs {
@@ -81,6 +93,72 @@ struct PriorArgs {
     int32_t mode;
     Geometry g;
 };
+
+// One AdamW step of one logit (section 3.4, Algorithm 1 "update logits"), in
+// fp32: m and v advance, z moves by lr (mh/(sqrt(vh)+eps) + wd z) with z the
+// value before this step.
+__device__ __forceinline__ void adam_step(float &z, float &m, float &v, float g, const Adam &a) {
+    m = __builtin_fmaf(a.b1, m, a.omb1 * g);
+    v = __builtin_fmaf(a.b2, v, a.omb2 * (g * g));
+    const float den = __builtin_sqrtf(v * a.ibc2) + a.eps;
+    const float upd = (m * a.ibc1) / den;
+    z = z - a.lr * __builtin_fmaf(a.wd, z, upd);
+}
+
+__device__ __forceinline__ void adam_step4(float4 &z, float4 &m, float4 &v, float4 g,
+                                           const Adam &a) {
+    adam_step(z.x, m.x, v.x, g.x, a);
+    adam_step(z.y, m.y, v.y, g.y, a);
+    adam_step(z.z, m.z, v.z, g.z, a);
+    adam_step(z.w, m.w, v.w, g.w, a);
+}
+
+// AdamW update of nf consecutive logits z[0..nf) (16-byte aligned, at most CAP
+// float4) whose gradients are at g[0..nf) in LDS, with their moments m1, m2.
+// Float4 number k*THREADS + t is handled by thread t; the loads of BATCH such
+// rounds are issued before any of them is used.  An odd float pair at the end
+// is handled by thread 0.  Every thread of the workgroup calls this after the
+// barrier that publishes g.
+template <int THREADS, int CAP, int BATCH>
+__device__ __forceinline__ void adamw_span(float *z, float *m1, float *m2, const float *g, int nf,
+                                           const Adam &a) {
+    const int t = threadIdx.x;
+    const int n4 = nf >> 2;
+    constexpr int kRounds = (CAP + THREADS - 1) / THREADS;
+    for (int r0 = 0; r0 < kRounds; r0 += BATCH) {
+        float4 zz[BATCH], mm[BATCH], vv[BATCH];
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+            const int i = (r0 + k) * THREADS + t;
+            if (i < n4) {
+                zz[k] = reinterpret_cast<const float4 *>(z)[i];
+                mm[k] = reinterpret_cast<const float4 *>(m1)[i];
+                vv[k] = reinterpret_cast<const float4 *>(m2)[i];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+            const int i = (r0 + k) * THREADS + t;
+            if (i < n4) {
+                adam_step4(zz[k], mm[k], vv[k], reinterpret_cast<const float4 *>(g)[i], a);
+                reinterpret_cast<float4 *>(z)[i] = zz[k];
+                reinterpret_cast<float4 *>(m1)[i] = mm[k];
+                reinterpret_cast<float4 *>(m2)[i] = vv[k];
+            }
+        }
+    }
+    if ((nf & 3) && t == 0) {
+        const int i = 2 * n4;
+        float2 zz = reinterpret_cast<float2 *>(z)[i], mm = reinterpret_cast<float2 *>(m1)[i];
+        float2 vv = reinterpret_cast<float2 *>(m2)[i];
+        const float2 gg = reinterpret_cast<const float2 *>(g)[i];
+        adam_step(zz.x, mm.x, vv.x, gg.x, a);
+        adam_step(zz.y, mm.y, vv.y, gg.y, a);
+        reinterpret_cast<float2 *>(z)[i] = zz;
+        reinterpret_cast<float2 *>(m1)[i] = mm;
+        reinterpret_cast<float2 *>(m2)[i] = vv;
+    }
+}
 
 int device_cu_count();
 

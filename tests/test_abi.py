@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert mg.maskgs_abi_version() == 1
+    assert mg.maskgs_abi_version() == 2
     for s in range(0, 10):
         assert isinstance(L.maskgs_status_str(s), bytes)
 
@@ -95,6 +95,35 @@ def test_bwd_reg_hard_prior_validation(L):
     assert L.maskgs_prior_init(bd, A + 1, A, None, 1, 3.0, 0, None) == mg.MASKGS_E_ALIGN
     assert L.maskgs_debug_philox(0, 0, 0, 0, -1, A, None) == mg.MASKGS_E_SHAPE
     assert L.maskgs_debug_gumbel(A, 4, None, None) == mg.MASKGS_E_NULL
+
+
+def test_bwd_adamw_validation(L):
+    d = mg.TensorDesc(2, 4, 8, 16, 0, 0)
+    p = mg.SampleParams(0, 0, 100.0, 4.0, 0)
+    bd, bp = ctypes.byref(d), ctypes.byref(p)
+
+    def call(opt, z=A, y=None, m1=A, m2=A, lam=1e-5, desc=bd):
+        o = None if opt is None else ctypes.byref(opt)
+        return L.maskgs_bwd_adamw(desc, bp, A, 1, z, y, A, 1, lam, m1, m2, o, None)
+
+    good = dict(lr=5e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1, t=1)
+    opt = lambda **kw: mg.AdamWParams(**{**good, **kw})
+    assert call(None) == mg.MASKGS_E_NULL
+    assert call(opt(), z=None) == mg.MASKGS_E_NULL          # z is always read and written
+    assert call(opt(), m1=None) == mg.MASKGS_E_NULL
+    assert call(opt(), m2=None) == mg.MASKGS_E_NULL
+    assert call(opt(lr=-1e-3)) == mg.MASKGS_E_RANGE
+    assert call(opt(beta1=1.0)) == mg.MASKGS_E_RANGE
+    assert call(opt(beta2=-0.1)) == mg.MASKGS_E_RANGE
+    assert call(opt(eps=0.0)) == mg.MASKGS_E_RANGE
+    assert call(opt(weight_decay=-0.1)) == mg.MASKGS_E_RANGE
+    assert call(opt(t=0)) == mg.MASKGS_E_RANGE
+    assert call(opt(lr=float("nan"))) == mg.MASKGS_E_RANGE
+    assert call(opt(), lam=-1.0) == mg.MASKGS_E_RANGE
+    assert call(opt(), m2=A + 4) == mg.MASKGS_E_ALIGN
+    # empty tensors launch nothing and succeed
+    e = mg.TensorDesc(4, 8, 0, 16, 0, 0)
+    assert call(opt(), z=None, m1=None, m2=None, desc=ctypes.byref(e)) == mg.MASKGS_OK
 
 
 def test_python_wrapper_refuses_cpu_tensors():
