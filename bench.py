@@ -8,7 +8,10 @@ index saved, regulariser reduced) with the hard mask of the same logits
 then the logit backward of every tensor (from the saved soft index).  The
 step's outputs equal those of forward, backward and a separate extraction
 pass; that unfused order is timed too and reported beside the step.  Prior
-seeding, an initialisation step, is timed once after the steps.
+seeding, an initialisation step, is timed once after the steps.  Then the
+training step with the logit update fused into the backward
+(maskgs_bwd_adamw) is timed with the soft index saved and recomputed, and
+reported under `train_step` (--no-train-step skips it).
 
 Prints ONE JSON line.  `value` = 2:4 weight blocks per second through the whole
 step; `roofline` describes the kernel with the largest share of the step;
@@ -45,6 +48,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=None,
                     help="use only the first L layers (profiling runs; default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-train-step", action="store_true",
+                    help="skip the training step with the fused AdamW update")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -257,6 +262,66 @@ def main():
     torch.cuda.synchronize()
     prior_ms = pe0.elapsed_time(pe1)
 
+    # ---- training step with the logit update fused in (AdamW) -------------
+    # maskgs_bwd_adamw keeps the logit gradient out of HBM, so the gradient
+    # buffers hold the first moments; the second moments are allocated here.
+    gb = 2 if wl.g_dtype == "bf16" else 4
+    train = {}
+    if not args.no_train_step:
+        vbufs = [torch.zeros_like(d["z"]) for d in bufs]
+        hp = mg.AdamWParams(5e-4, 0.9, 0.999, 1e-8, 0.1, 1)
+        hpref = ctypes.byref(hp)
+        modes = {
+            # bytes per block: fwd_hard (W, z in; out, hard outputs, y out) and
+            # bwd_adamw (W, G, y or z in; z, m, v in and out)
+            "saved_y": (per_block_bytes["fwd_hard"], M * wb + M * gb + 4 * K + 24 * K),
+            "recompute_y": (per_block_bytes["fwd_hard"] - 4 * K, M * wb + M * gb + 24 * K),
+        }
+        for mode, (fb, bb) in modes.items():
+            seq = []
+            for d, v in zip(bufs, vbufs):
+                yp = ptr(d["y"]) if mode == "saved_y" else None
+                dref = ctypes.byref(d["desc"])
+                seq.append(("fwd_hard", L.maskgs_fwd_hard,
+                            (dref, pref, ptr(d["w"]), bf, ptr(d["z"]), ptr(d["out"]), bf, yp,
+                             ptr(reg), None, ptr(d["bits"]), ptr(d["vals"]), ptr(d["vidx"]),
+                             sptr)))
+            for d, v in zip(bufs, vbufs):
+                yp = ptr(d["y"]) if mode == "saved_y" else None
+                dref = ctypes.byref(d["desc"])
+                seq.append(("bwd_adamw", L.maskgs_bwd_adamw,
+                            (dref, pref, ptr(d["w"]), bf, ptr(d["z"]), yp, ptr(d["G"]), gdt,
+                             ctypes.c_float(wl.lam), ptr(d["dz"]), ptr(v), hpref, sptr)))
+            ph = {"fwd_hard": [], "bwd_adamw": []}
+            t0, t1 = ev(), ev()
+            torch.cuda.synchronize()
+            t0.record(stream)
+            for s_ in range(args.steps):
+                params[0].step = s_
+                hp.t = s_ + 1
+                reg.zero_()
+                for kind in ("fwd_hard", "bwd_adamw"):
+                    p0, p1 = ev(), ev()
+                    p0.record(stream)
+                    for k_, fn, a in seq:
+                        if k_ == kind:
+                            rc = fn(*a)
+                            if rc != 0:
+                                raise RuntimeError(f"{kind}: status {rc}")
+                    p1.record(stream)
+                    ph[kind].append((p0, p1))
+            t1.record(stream)
+            torch.cuda.synchronize()
+            ms_t = t0.elapsed_time(t1) / args.steps
+            ks = {}
+            for kind, bpb in (("fwd_hard", fb), ("bwd_adamw", bb)):
+                tot = sum(a.elapsed_time(b) for a, b in ph[kind]) / args.steps
+                ks[kind] = dict(ms_per_step=round(tot, 4), algorithmic_bytes_per_block=bpb,
+                                achieved_gbs=round(bpb * total_blocks / (tot * 1e-3) / 1e9, 1))
+            train[mode] = dict(ms_per_step=round(ms_t, 3),
+                               value=round(total_blocks / (ms_t * 1e-3), 1), kernels=ks)
+        del vbufs
+
     if args.calibrate_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
@@ -299,6 +364,12 @@ def main():
                                              1)},
         "roofline": roofline,
     }
+    if train:
+        result["train_step"] = {
+            "what": "fwd with the hard mask fused in, then maskgs_bwd_adamw (backward fused with "
+                    "the AdamW update of the logits: lr 5e-4, betas 0.9/0.999, eps 1e-8, "
+                    "weight decay 0.1); the logit gradient never reaches HBM",
+            **train}
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, bufs, mg)
