@@ -78,6 +78,8 @@ def lib():
     L.orc_hard_extract.argtypes = [c.c_int, c.c_int, c.c_int64, c.c_int64, P, P, c.c_int,
                                    P, P, P, P]
     L.orc_hard_extract.restype = c.c_int
+    L.orc_sample_logits.argtypes = common + [P, P]
+    L.orc_sample_logits.restype = c.c_int
     L.orc_adamw.argtypes = [c.c_int64, P, P, P, P, c.c_double, c.c_double, c.c_double,
                             c.c_double, c.c_double, c.c_uint32]
     L.orc_adamw.restype = c.c_int
@@ -220,6 +222,67 @@ def adamw(z, g, m, v, *, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1,
     if rc != 0:
         raise ValueError("oracle adamw: invalid arguments")
     return z, m, v
+
+
+def sample_logits(n, m, z, rows, cols, *, kappa, tau, seed=0, step=0, tensor_id=0,
+                  block_offset=0, flags=0):
+    """The perturbed, tempered logits a_i = fp32(fp32(kappa z_i + g_i) fp32(1/tau))
+    of every block, fp32 [B, K] (the argument of Eq. 6's softmax)."""
+    B = rows * (cols // m)
+    K = len(candidates(n, m))
+    z = _f32(z).reshape(B, K)
+    a = np.zeros((B, K), dtype=np.float32)
+    rc = lib().orc_sample_logits(n, m, rows, cols, block_offset, tensor_id, seed, step, kappa,
+                                 tau, flags, _ptr(z), _ptr(a))
+    if rc != 0:
+        raise ValueError("oracle sample_logits: invalid arguments")
+    return a
+
+
+def unpack_masks(bits, nblocks, m):
+    """Per-block masks (uint8 bitmasks) from the packed LSB-first stream."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint8)
+    allbits = np.unpackbits(bits, bitorder="little")[: nblocks * m].reshape(nblocks, m)
+    return (allbits.astype(np.uint32) << np.arange(m, dtype=np.uint32)).sum(axis=1).astype(np.uint8)
+
+
+def mask_stats(n, m, z, rows, cols, *, kappa, ref_bits=None, w=None, dz=None, sample=None):
+    """Training diagnostics of one tensor, as sums over its blocks (MaskLLM
+    summary, section 3.4 kappa discussion / Figure 5, Figure 6, Figure 8,
+    Table 14):
+      blocks        number of blocks;
+      changed       blocks whose hard mask differs from ref_bits (packed);
+      max_prob      sum over blocks of max_i softmax(kappa z)_i (fp64);
+      kept_l1       sum of |w| at the hard mask's kept positions;
+      magnitude_l1  sum of |w| at the magnitude top-n positions;
+      grad_sq       sum of dz^2 over all logits (fp64).
+    The hard mask is S[first argmax_i z_i], or with sample = dict(tau=..., seed=...,
+    step=..., tensor_id=..., block_offset=..., flags=...) the Gumbel-max sample
+    S[first argmax_i a_i] of the noise contract.  w: fp32 values [rows, cols]."""
+    B = rows * (cols // m)
+    cands = candidates(n, m)
+    K = len(cands)
+    z = _f32(z).reshape(B, K)
+    key = z if sample is None else sample_logits(n, m, z, rows, cols, kappa=kappa, **sample)
+    hard = cands[np.argmax(key, axis=1)]          # first maximum per block
+    out = dict(blocks=B, changed=0, max_prob=0.0, kept_l1=0.0, magnitude_l1=0.0, grad_sq=0.0)
+    if ref_bits is not None:
+        out["changed"] = int((unpack_masks(ref_bits, B, m) != hard).sum())
+    z64 = z.astype(np.float64)
+    e = np.exp(float(kappa) * (z64 - z64.max(axis=1, keepdims=True)))
+    out["max_prob"] = float((1.0 / e.sum(axis=1)).sum())
+    if w is not None:
+        aw = np.abs(_f32(w).astype(np.float64)).reshape(B, m)
+        pos = np.arange(m, dtype=np.uint32)
+        keep = ((hard[:, None].astype(np.uint32) >> pos) & 1).astype(bool)
+        out["kept_l1"] = float(aw[keep].sum())
+        mag = unpack_masks(magnitude_mask(n, m, w), B, m)
+        keep_mag = ((mag[:, None].astype(np.uint32) >> pos) & 1).astype(bool)
+        out["magnitude_l1"] = float(aw[keep_mag].sum())
+    if dz is not None:
+        d = _f32(dz).astype(np.float64)
+        out["grad_sq"] = float((d * d).sum())
+    return out
 
 
 def hard_extract(n, m, z, rows, cols, w_raw=None):

@@ -236,8 +236,10 @@ static int orc_setup(orc_ctx *c, int n, int m, int64_t rows, int64_t cols, uint6
 /* Soft index of one block (MaskLLM summary, section 3.4, Eq. 6 and
  * Algorithm 1 steps 1-2): y_i = exp(a_i) / sum_j exp(a_j), a_i = (pi_i*kappa +
  * g_i)/tau.  Local block b has global index block_offset + b. */
-static void orc_soft_index(const orc_ctx *c, int64_t b, const float *zb, double *y) {
-    double a[ORC_MAX_K] = {0.0};
+/* Perturbed, tempered logits of block b (Eq. 6 argument, Algorithm 1):
+ * a_i = fp32(fp32(kappa*z_i + g_i) * fp32(1/tau)), or (kappa*z_i + g_i)/tau in
+ * fp64 under ORC_EXACT_LOGITS. */
+static void orc_logits(const orc_ctx *c, int64_t b, const float *zb, double *a) {
     uint64_t gb = c->block_offset + (uint64_t)b;
     float tau_inv = 1.0f / c->tau;
     for (int i = 0; i < c->k; ++i) {
@@ -250,6 +252,11 @@ static void orc_soft_index(const orc_ctx *c, int64_t b, const float *zb, double 
         else
             a[i] = (double)(fmaf(c->kappa, zb[i], g) * tau_inv);
     }
+}
+
+static void orc_soft_index(const orc_ctx *c, int64_t b, const float *zb, double *y) {
+    double a[ORC_MAX_K] = {0.0};
+    orc_logits(c, b, zb, a);
     double amax = a[0];
     for (int i = 1; i < c->k; ++i)
         if (a[i] > amax) amax = a[i];
@@ -545,6 +552,26 @@ int orc_adamw(int64_t count, float *z, const float *g, float *m, float *v, doubl
         z[i] = (float)zn;
         m[i] = (float)mi;
         v[i] = (float)vi;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* The perturbed, tempered logits a of every block ([B, K], the fp32 values  */
+/* of the noise contract); their first argmax is the Gumbel-max sample of    */
+/* the block's mask (section 3.4, Eq. 5).                                    */
+/* ------------------------------------------------------------------------- */
+int orc_sample_logits(int n, int m, int64_t rows, int64_t cols, uint64_t block_offset,
+                      uint32_t tensor_id, uint64_t seed, uint32_t step, float kappa, float tau,
+                      uint32_t flags, const float *z, float *a_out) {
+    orc_ctx c;
+    if (orc_setup(&c, n, m, rows, cols, block_offset, tensor_id, seed, step, kappa, tau, flags))
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < c.nblocks; ++b) {
+        double a[ORC_MAX_K];
+        orc_logits(&c, b, z + b * c.k, a);
+        for (int i = 0; i < c.k; ++i) a_out[b * c.k + i] = (float)a[i];
     }
     return 0;
 }

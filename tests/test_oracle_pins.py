@@ -627,3 +627,69 @@ def test_adamw_degenerate_cases(orc):
     # decay alone shrinks z by the factor (1 - lr wd)
     zo, _, _ = orc.adamw(z, zero, zero, zero, lr=5e-4, weight_decay=0.1, t=4)
     assert np.array_equal(zo, (z.astype(np.float64) * (1 - 5e-5)).astype(np.float32))
+
+
+# --------------------------------------------------------------------------
+# Training diagnostics (section 3.4 kappa discussion / Figure 5, Figure 6,
+# Figure 8, Table 14)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("nm", [(2, 4), (4, 8)])
+def test_sample_logits_are_the_soft_index_argument(orc, nm):
+    """softmax(a) of the exported perturbed logits is the pinned soft index."""
+    n, m = nm
+    w, z, _ = _rand_inputs(6, 8 * m, n, m, seed=21)
+    kw = dict(kappa=100.0, tau=2.0, seed=5, step=3, tensor_id=2, block_offset=7)
+    a = orc.sample_logits(n, m, z, 6, 8 * m, **kw).astype(np.float64)
+    y = np.exp(a - a.max(axis=1, keepdims=True))
+    y /= y.sum(axis=1, keepdims=True)
+    assert np.allclose(y, orc.fwd(n, m, w, z, **kw)["y"], rtol=1e-12, atol=1e-300)
+
+
+@pytest.mark.parametrize("nm", [(2, 4), (4, 8)])
+def test_mask_stats_closed_forms(orc, nm):
+    n, m = nm
+    rows, cols = 32, 16 * m
+    w, z, _ = _rand_inputs(rows, cols, n, m, seed=22)
+    B, K = z.shape
+    h = orc.hard_extract(n, m, z, rows, cols)
+    s = orc.mask_stats(n, m, z, rows, cols, kappa=100.0, ref_bits=h["bits"], w=w)
+    assert s["blocks"] == B and s["changed"] == 0
+    # every block's mask differs from its complement
+    s = orc.mask_stats(n, m, z, rows, cols, kappa=100.0, ref_bits=h["bits"] ^ 0xFF)
+    assert s["changed"] == B
+    # magnitude top-n keeps the largest |w| of each block: never less than the
+    # learned mask, and equal when the logits follow the magnitude prior
+    s = orc.mask_stats(n, m, z, rows, cols, kappa=100.0, w=w)
+    assert s["kept_l1"] <= s["magnitude_l1"] and s["kept_l1"] < s["magnitude_l1"]
+    zp = orc.prior_init(n, m, np.zeros_like(z), rows, cols, alpha=1.0, mode=1, w=w)
+    s = orc.mask_stats(n, m, zp, rows, cols, kappa=100.0, w=w)
+    assert s["kept_l1"] == s["magnitude_l1"]
+    # maximum probability: uniform for constant logits, one-hot for large kappa
+    s = orc.mask_stats(n, m, np.full_like(z, 0.3), rows, cols, kappa=100.0)
+    assert abs(s["max_prob"] - B / K) < 1e-9 * B
+    s = orc.mask_stats(n, m, z, rows, cols, kappa=1e6)
+    assert abs(s["max_prob"] - B) < 1e-6 * B
+    # gradient norm: constant gradient c over B*K logits
+    s = orc.mask_stats(n, m, z, rows, cols, kappa=1.0, dz=np.full_like(z, 0.125))
+    assert s["grad_sq"] == B * K * 0.125 ** 2
+
+
+def test_mask_change_between_steps_follows_kappa(orc):
+    """Figure 5: with the noise dominating (tiny kappa) the sampled masks of two
+    steps are independent draws from a near-uniform distribution and differ in
+    a fraction 1 - 1/K of the blocks; with the logits dominating they agree."""
+    n, m = 2, 4
+    rows, cols = 256, 256
+    w, z, _ = _rand_inputs(rows, cols, n, m, seed=23, zstd=0.01)
+    B, K = z.shape
+    for kappa, expect in [(1e-3, 1 - 1 / K), (1e5, 0.0)]:
+        s0 = dict(tau=1.0, seed=4, step=0, tensor_id=0, block_offset=0)
+        a0 = orc.sample_logits(n, m, z, rows, cols, kappa=kappa, **s0)
+        cands = orc.candidates(n, m)
+        bits0 = np.packbits(((cands[np.argmax(a0, axis=1)][:, None] >> np.arange(m)) & 1)
+                            .astype(np.uint8).reshape(-1), bitorder="little")
+        st = orc.mask_stats(n, m, z, rows, cols, kappa=kappa, ref_bits=bits0,
+                            sample=dict(s0, step=1))
+        frac = st["changed"] / B
+        sd = math.sqrt(expect * (1 - expect) / B) + 1e-12
+        assert abs(frac - expect) <= 5 * sd + (0.002 if expect == 0 else 0), (kappa, frac)
