@@ -180,6 +180,42 @@ int maskgs_bwd_adamw(const maskgs_tensor_desc *t, const maskgs_sample_params *p,
                      maskgs_dtype dout_dt, float lambda, float *exp_avg, float *exp_avg_sq,
                      const maskgs_adamw_params *opt, hipStream_t stream);
 
+/* Training diagnostics of one tensor, as sums that maskgs_mask_stats adds to a
+ * DEVICE struct (the caller zeroes it; tensors and steps accumulate).  They are
+ * the quantities the pages plot: the mask change between training steps and
+ * the maximum probability of the learned distribution (section 3.4, kappa
+ * discussion, Figure 5), the weight norm the mask keeps against magnitude
+ * pruning (Figure 6), the mask difference between two masks (Figure 8) and the
+ * logit gradient norm (Table 14). */
+typedef struct {
+    uint64_t blocks;     /* blocks counted                                        */
+    uint64_t changed;    /* blocks whose hard mask differs from ref_bits          */
+    double max_prob;     /* sum over blocks of max_i softmax(kappa z)_i           */
+    double kept_l1;      /* sum of |w| at the kept positions of the hard mask     */
+    double magnitude_l1; /* sum of |w| at the magnitude top-n positions           */
+    double grad_sq;      /* sum of dz^2 over all logits                           */
+} maskgs_stats;
+
+/* Adds the diagnostics of one tensor to *stats (device, 16-byte aligned):
+ *   z        [B, K] logits (required).  The hard mask of block b is S[k_b],
+ *            k_b the first index of the largest z_b,i, or, when sample is not
+ *            NULL, the first index of the largest perturbed logit
+ *            a_i = fp32(fp32(kappa z_i + g_i) fp32(1/tau)) of that draw (the
+ *            Gumbel-max sample, section 3.4 Eq. 5; block_offset and tensor_id of
+ *            t select the noise as in maskgs_fwd).
+ *   kappa    >= 0, the scale of max_prob's softmax(kappa z).
+ *   ref_bits NULL, or packed masks (maskgs_hard_extract's mask_bits format):
+ *            changed counts the blocks whose hard mask differs.
+ *   w        NULL, or the weight [rows, cols] of w_dt: kept_l1 and magnitude_l1
+ *            (magnitude top-n as in maskgs_prior_init).
+ *   dz       NULL, or [B, K] fp32 logit gradients: grad_sq.
+ * max_prob always accumulates; blocks counts every block of t.  The sums use
+ * device atomics, so their fp64 rounding order varies between runs. */
+int maskgs_mask_stats(const maskgs_tensor_desc *t, const float *z, float kappa,
+                      const maskgs_sample_params *sample, const uint8_t *ref_bits, const void *w,
+                      maskgs_dtype w_dt, const float *dz, maskgs_stats *stats,
+                      hipStream_t stream);
+
 /* Regulariser value alone (section 3.4, Eq. 8): adds sum_b ||W_b (.) M~_b||^2 to
  * *reg_accum (one device double, atomically) without writing W (.) M~.
  * y_saved as in maskgs_bwd. */

@@ -35,7 +35,7 @@ MASKGS_NO_NOISE = 1
 
 EXPORTS = ("maskgs_abi_version", "maskgs_status_str", "maskgs_candidates", "maskgs_fwd",
            "maskgs_fwd_hard",
-           "maskgs_bwd", "maskgs_bwd_adamw", "maskgs_reg_reduce", "maskgs_hard_extract", "maskgs_prior_init",
+           "maskgs_bwd", "maskgs_bwd_adamw", "maskgs_mask_stats", "maskgs_reg_reduce", "maskgs_hard_extract", "maskgs_prior_init",
            "maskgs_debug_philox", "maskgs_debug_gumbel")
 
 
@@ -89,6 +89,8 @@ def load_library(path: str = LIB_PATH):
     L.maskgs_bwd.argtypes = [DP, SP, P, c.c_int, P, P, P, c.c_int, c.c_float, P, c.c_int32, P]
     L.maskgs_bwd_adamw.argtypes = [DP, SP, P, c.c_int, P, P, P, c.c_int, c.c_float, P, P,
                                    c.POINTER(AdamWParams), P]
+    L.maskgs_mask_stats.argtypes = [DP, P, c.c_float, c.POINTER(SampleParams), P, P, c.c_int, P,
+                                    P, P]
     L.maskgs_reg_reduce.argtypes = [DP, SP, P, c.c_int, P, P, P, P]
     L.maskgs_hard_extract.argtypes = [DP, P, P, c.c_int, P, P, P, P, P]
     L.maskgs_prior_init.argtypes = [DP, P, P, P, c.c_int, c.c_float, c.c_int32, P]
@@ -262,6 +264,41 @@ def maskgs_bwd_adamw(t: Tensor, p: SampleParams, w, z, y_saved, dout, lam: float
         _ptr(exp_avg_sq, "exp_avg_sq", f32, t.nblocks * t.k, dev), ctypes.byref(opt),
         _stream(stream)))
     return z
+
+
+STATS_FIELDS = ("blocks", "changed", "max_prob", "kept_l1", "magnitude_l1", "grad_sq")
+
+
+def new_stats(device):
+    """A zeroed device maskgs_stats (48 bytes) for maskgs_mask_stats."""
+    return _torch().zeros(6, dtype=_torch().int64, device=device)
+
+
+def read_stats(stats) -> dict:
+    """The maskgs_stats fields of a device buffer from new_stats()."""
+    host = stats.detach().cpu()
+    f = host[2:].view(_torch().float64)
+    return dict(blocks=int(host[0]), changed=int(host[1]), max_prob=float(f[0]),
+                kept_l1=float(f[1]), magnitude_l1=float(f[2]), grad_sq=float(f[3]))
+
+
+def maskgs_mask_stats(t: Tensor, z, kappa: float, stats, sample: SampleParams = None,
+                      ref_bits=None, w=None, dz=None, stream=None):
+    """Adds one tensor's training diagnostics (mask change, maximum probability,
+    kept-weight norm vs magnitude, gradient norm; section 3.4 Figure 5, Figures
+    6 and 8, Table 14) to `stats` (from new_stats)."""
+    torch = _torch()
+    dev = z.device
+    B = t.nblocks
+    w_dt = _dtype_code(w) if w is not None else MASKGS_BF16
+    _check("maskgs_mask_stats", load_library().maskgs_mask_stats(
+        ctypes.byref(t.desc()), _ptr(z, "z", torch.float32, B * t.k, dev), float(kappa),
+        None if sample is None else ctypes.byref(sample),
+        _ptr(ref_bits, "ref_bits", torch.uint8, (B * t.m + 7) // 8, dev),
+        _ptr(w, "w", numel=t.rows * t.cols, device=dev), w_dt,
+        _ptr(dz, "dz", torch.float32, B * t.k, dev),
+        _ptr(stats, "stats", torch.int64, 6, dev), _stream(stream)))
+    return stats
 
 
 def maskgs_reg_reduce(t: Tensor, p: SampleParams, w, z, y_saved, reg_accum, stream=None):

@@ -219,6 +219,28 @@ int maskgs_bwd_adamw(const maskgs_tensor_desc *t, const maskgs_sample_params *p,
     return launch_status(launch_bwd48(a, w_dt, dout_dt, stream));
 }
 
+int maskgs_mask_stats(const maskgs_tensor_desc *t, const float *z, float kappa,
+                      const maskgs_sample_params *sample, const uint8_t *ref_bits, const void *w,
+                      maskgs_dtype w_dt, const float *dz, maskgs_stats *stats,
+                      hipStream_t stream) {
+    Geometry g;
+    Noise nz{};
+    int rc = check_desc(t, &g);
+    if (rc) return rc;
+    if (sample && (rc = check_params(sample, &nz))) return rc;
+    if (!std::isfinite(kappa) || kappa < 0.0f) return MASKGS_E_RANGE;
+    if (!stats) return MASKGS_E_NULL;
+    if (misaligned(stats)) return MASKGS_E_ALIGN;
+    if (g.nblocks == 0) return MASKGS_OK;
+    if (!z) return MASKGS_E_NULL;
+    if (w && !valid_dtype(w_dt)) return MASKGS_E_DTYPE;
+    if (misaligned(z) || misaligned(ref_bits) || misaligned(w) || misaligned(dz))
+        return MASKGS_E_ALIGN;
+    StatsArgs a{z, ref_bits, w, dz, stats, kappa * 1.44269504088896341f, g, nz};
+    if (g.m == 4) return launch_status(launch_stats24(a, sample != nullptr, w_dt, stream));
+    return launch_status(launch_stats48(a, sample != nullptr, w_dt, stream));
+}
+
 int maskgs_reg_reduce(const maskgs_tensor_desc *t, const maskgs_sample_params *p, const void *w,
                       maskgs_dtype w_dt, const float *z, const float *y_saved,
                       double *reg_accum, hipStream_t stream) {

@@ -305,19 +305,25 @@ __device__ __forceinline__ void hard_pair(uint8_t *idx, uint8_t *bits, void *val
 // The noise flag is uniform, so the twelve Gumbel evaluations form one
 // straight-line block the scheduler can interleave.
 template <int PHASE>
+__device__ __forceinline__ void pair_logits(const Geometry &g, const Noise &nz, int64_t p,
+                                            const float (&z)[12], float (&a12)[12]) {
+    if (nz.no_noise) {
+#pragma unroll
+        for (int i = 0; i < 12; ++i) a12[i] = __builtin_fmaf(nz.kappa, z[i], 0.0f) * nz.tau_inv;
+    } else {
+        uint32_t wd[12];
+        pair_words<PHASE>(g, nz, p, wd);
+#pragma unroll
+        for (int i = 0; i < 12; ++i)
+            a12[i] = __builtin_fmaf(nz.kappa, z[i], -neg_gumbel(wd[i])) * nz.tau_inv;
+    }
+}
+
+template <int PHASE>
 __device__ __forceinline__ void pair_soft_index(const FwdArgs &a, int64_t p, const float (&z)[12],
                                                 float (&y)[12]) {
     float a12[12];
-    if (a.nz.no_noise) {
-#pragma unroll
-        for (int i = 0; i < 12; ++i) a12[i] = __builtin_fmaf(a.nz.kappa, z[i], 0.0f) * a.nz.tau_inv;
-    } else {
-        uint32_t wd[12];
-        pair_words<PHASE>(a.g, a.nz, p, wd);
-#pragma unroll
-        for (int i = 0; i < 12; ++i)
-            a12[i] = __builtin_fmaf(a.nz.kappa, z[i], -neg_gumbel(wd[i])) * a.nz.tau_inv;
-    }
+    pair_logits<PHASE>(a.g, a.nz, p, z, a12);
     softmax6(a12, y);
     softmax6(a12 + 6, y + 6);
 }
@@ -610,6 +616,116 @@ __global__ __launch_bounds__(kThreads) void prior24_kernel(PriorArgs a) {
 // ---------------------------------------------------------------------------
 // Launch helpers.
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Training diagnostics (section 3.4 kappa discussion / Figure 5, Figures 6 and
+// 8, Table 14): per-lane sums over block pairs, one set of atomics per
+// workgroup.
+// ---------------------------------------------------------------------------
+// max_i softmax(kappa z)_i of one block = 1 / sum_i exp(kappa (z_i - zmax)).
+__device__ __forceinline__ float max_prob6(const float *z, float kappa_log2e) {
+    float zmax = z[0];
+#pragma unroll
+    for (int i = 1; i < 6; ++i) zmax = fmaxf(zmax, z[i]);
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) s += __builtin_amdgcn_exp2f((z[i] - zmax) * kappa_log2e);
+    return 1.0f / s;
+}
+
+// Sum of |w| over the positions kept by `keep` (bit j = position j).
+__device__ __forceinline__ double kept_abs4(const float *w, uint32_t keep) {
+    double s = 0.0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if ((keep >> j) & 1u) s += static_cast<double>(fabsf(w[j]));
+    return s;
+}
+
+// Workgroup sums of five per-lane values; thread 0 adds them to the stats.
+__device__ __forceinline__ void stats_flush(double (&v)[5], maskgs_stats *st) {
+    __shared__ double part[5][kThreads / 64];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) v[k] += __shfl_xor(v[k], off);
+        if (lane == 0) part[k][wid] = v[k];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int k = 0; k < 5; ++k)
+#pragma unroll
+            for (int i = 0; i < kThreads / 64; ++i) t[k] += part[k][i];
+        if (t[0] != 0.0)
+            atomicAdd(reinterpret_cast<unsigned long long *>(&st->changed),
+                      static_cast<unsigned long long>(t[0]));
+        atomicAdd(&st->max_prob, t[1]);
+        if (t[2] != 0.0 || t[3] != 0.0) {
+            atomicAdd(&st->kept_l1, t[2]);
+            atomicAdd(&st->magnitude_l1, t[3]);
+        }
+        if (t[4] != 0.0) atomicAdd(&st->grad_sq, t[4]);
+    }
+}
+
+template <int PHASE, typename WT, bool SAMPLED>
+__global__ __launch_bounds__(kThreads) void stats24_kernel(StatsArgs a) {
+    const int64_t npairs = (a.g.nblocks + 1) >> 1;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    double acc[5] = {0.0, 0.0, 0.0, 0.0, 0.0};  // changed, max_prob, kept, magnitude, grad^2
+    for (int64_t p = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; p < npairs;
+         p += stride) {
+        const bool two = 2 * p + 1 < a.g.nblocks;
+        float z[12];
+        load12(a.z, p, two, z);
+        int k0, k1;
+        if (SAMPLED) {
+            float a12[12];
+            pair_logits<PHASE>(a.g, a.nz, p, z, a12);
+            k0 = first_argmax6(a12);
+            k1 = first_argmax6(a12 + 6);
+        } else {
+            k0 = first_argmax6(z);
+            k1 = first_argmax6(z + 6);
+        }
+        const uint32_t m0 = cand_mask6(k0), m1 = cand_mask6(k1);
+        if (a.ref_bits) {
+            const uint32_t rb = a.ref_bits[p];
+            acc[0] += static_cast<double>(((rb & 0xFu) != m0) + (two && ((rb >> 4) != m1)));
+        }
+        acc[1] += static_cast<double>(max_prob6(z, a.kappa_log2e));
+        if (two) acc[1] += static_cast<double>(max_prob6(z + 6, a.kappa_log2e));
+        if (a.w) {
+            float w[8];
+            uint32_t r[8], mag[8];
+            Io<WT>::load8(a.w, p, two, w);
+            Io<WT>::load8_raw(a.w, p, two, r);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) mag[j] = Io<WT>::magnitude(r[j]);
+            acc[2] += kept_abs4(w, m0);
+            acc[3] += kept_abs4(w, top2_of4(mag));
+            if (two) {
+                acc[2] += kept_abs4(w + 4, m1);
+                acc[3] += kept_abs4(w + 4, top2_of4(mag + 4));
+            }
+        }
+        if (a.dz) {
+            float d[12];
+            load12(a.dz, p, two, d);
+            double s = 0.0;
+#pragma unroll
+            for (int i = 0; i < 12; ++i) s += static_cast<double>(d[i]) * static_cast<double>(d[i]);
+            acc[4] += s;
+        }
+    }
+    stats_flush(acc, a.stats);
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        atomicAdd(reinterpret_cast<unsigned long long *>(&a.stats->blocks),
+                  static_cast<unsigned long long>(a.g.nblocks));
+}
+
 template <typename K, typename A>
 hipError_t go(K kernel, const A &args, int64_t items, hipStream_t s) {
     const unsigned grid = grid_for(items, kThreads, kWavesPerCU);
@@ -688,6 +804,21 @@ hipError_t launch_prior24(const PriorArgs &a, maskgs_dtype w_dt, hipStream_t s) 
     if (a.prior_bits) return go(prior24_kernel<bf16_t, true>, a, np, s);
     if (w_dt == MASKGS_F32) return go(prior24_kernel<float, false>, a, np, s);
     return go(prior24_kernel<bf16_t, false>, a, np, s);
+}
+
+template <int PHASE>
+hipError_t stats24_dispatch(const StatsArgs &a, bool sampled, maskgs_dtype w_dt, hipStream_t s) {
+    const int64_t np = (a.g.nblocks + 1) >> 1;
+    if (sampled)
+        return w_dt == MASKGS_F32 ? go(stats24_kernel<PHASE, float, true>, a, np, s)
+                                  : go(stats24_kernel<PHASE, bf16_t, true>, a, np, s);
+    return w_dt == MASKGS_F32 ? go(stats24_kernel<PHASE, float, false>, a, np, s)
+                              : go(stats24_kernel<PHASE, bf16_t, false>, a, np, s);
+}
+
+hipError_t launch_stats24(const StatsArgs &a, bool sampled, maskgs_dtype w_dt, hipStream_t s) {
+    return phase_of(a.g.block_offset) == 0 ? stats24_dispatch<0>(a, sampled, w_dt, s)
+                                           : stats24_dispatch<2>(a, sampled, w_dt, s);
 }
 
 }  // namespace maskgs

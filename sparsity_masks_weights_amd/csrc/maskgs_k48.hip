@@ -674,6 +674,97 @@ __global__ __launch_bounds__(kWave) void prior48_kernel(PriorArgs a) {
 // ---------------------------------------------------------------------------
 // Launch helpers.
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Training diagnostics (section 3.4 kappa discussion / Figure 5, Figures 6 and
+// 8, Table 14): per-lane sums over the blocks of each tile, one set of atomics
+// per wave.
+// ---------------------------------------------------------------------------
+template <typename WT, bool SAMPLED>
+__global__ __launch_bounds__(kWave) void stats48_kernel(StatsArgs a) {
+    __shared__ float4 tile4[kWave * kK / 4];
+    const float *tl = reinterpret_cast<const float *>(tile4);
+    const int lane = threadIdx.x;
+    const int64_t ntiles = tile_count(a.g.nblocks);
+    double acc[5] = {0.0, 0.0, 0.0, 0.0, 0.0};  // changed, max_prob, kept, magnitude, grad^2
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t b0 = tile * kWave;
+        const int nb = static_cast<int>(a.g.nblocks - b0 < kWave ? a.g.nblocks - b0 : kWave);
+        const int64_t b = b0 + lane;
+        tile_copy_in(a.z, b0, nb, reinterpret_cast<float *>(tile4));
+        lds_fill_wait();
+        __syncthreads();
+        if (lane < nb) {
+            const float *row = tl + lane * kK;
+            uint32_t key;
+            if (SAMPLED) {
+                float v[kK];
+#pragma unroll
+                for (int i = 0; i < kK; ++i) v[i] = row[i];
+                logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz);
+                key = argmax_key70(v);
+            } else {
+                key = argmax_key70(row);
+            }
+            const uint32_t mask = key & 0xFFu;
+            if (a.ref_bits) acc[0] += static_cast<double>(a.ref_bits[b] != mask);
+            float zmax = row[0];
+#pragma unroll
+            for (int i = 1; i < kK; ++i) zmax = fmaxf(zmax, row[i]);
+            float s = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kK; ++i) s += __builtin_amdgcn_exp2f((row[i] - zmax) * a.kappa_log2e);
+            acc[1] += static_cast<double>(1.0f / s);
+            if (a.w) {
+                float w[8];
+                uint32_t mag[8];
+                Io8<WT>::load(a.w, b, w);
+                Io8<WT>::load_mag(a.w, b, mag);
+                const uint32_t top = top4_of8(mag);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const double aw = static_cast<double>(fabsf(w[j]));
+                    if ((mask >> j) & 1u) acc[2] += aw;
+                    if ((top >> j) & 1u) acc[3] += aw;
+                }
+            }
+        }
+        if (a.dz) {
+            // the tile's gradients, coalesced
+            const float *src = a.dz + b0 * kK;
+            const int nf = nb * kK, n4 = nf >> 2;
+            for (int i = lane; i < n4; i += kWave) {
+                const float4 d = reinterpret_cast<const float4 *>(src)[i];
+                acc[4] += static_cast<double>(d.x) * d.x + static_cast<double>(d.y) * d.y +
+                          static_cast<double>(d.z) * d.z + static_cast<double>(d.w) * d.w;
+            }
+            if ((nf & 3) && lane == 0) {
+                const float2 d = reinterpret_cast<const float2 *>(src)[2 * n4];
+                acc[4] += static_cast<double>(d.x) * d.x + static_cast<double>(d.y) * d.y;
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int k = 0; k < 5; ++k)
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) acc[k] += __shfl_xor(acc[k], off);
+    if (lane == 0) {
+        maskgs_stats *st = a.stats;
+        if (acc[0] != 0.0)
+            atomicAdd(reinterpret_cast<unsigned long long *>(&st->changed),
+                      static_cast<unsigned long long>(acc[0]));
+        atomicAdd(&st->max_prob, acc[1]);
+        if (acc[2] != 0.0 || acc[3] != 0.0) {
+            atomicAdd(&st->kept_l1, acc[2]);
+            atomicAdd(&st->magnitude_l1, acc[3]);
+        }
+        if (acc[4] != 0.0) atomicAdd(&st->grad_sq, acc[4]);
+        if (blockIdx.x == 0)
+            atomicAdd(reinterpret_cast<unsigned long long *>(&st->blocks),
+                      static_cast<unsigned long long>(a.g.nblocks));
+    }
+}
+
 template <typename Kern, typename A>
 hipError_t go(Kern kernel, const A &args, int64_t nblocks, hipStream_t s) {
     const unsigned grid = grid_for((nblocks + kWave - 1) / kWave, 1, kWgPerCU);
@@ -735,6 +826,15 @@ hipError_t launch_prior48(const PriorArgs &a, maskgs_dtype w_dt, hipStream_t s) 
     if (a.prior_bits) return go(prior48_kernel<bf16_t, true>, a, n, s);
     if (w_dt == MASKGS_F32) return go(prior48_kernel<float, false>, a, n, s);
     return go(prior48_kernel<bf16_t, false>, a, n, s);
+}
+
+hipError_t launch_stats48(const StatsArgs &a, bool sampled, maskgs_dtype w_dt, hipStream_t s) {
+    const int64_t n = a.g.nblocks;
+    if (sampled)
+        return w_dt == MASKGS_F32 ? go(stats48_kernel<float, true>, a, n, s)
+                                  : go(stats48_kernel<bf16_t, true>, a, n, s);
+    return w_dt == MASKGS_F32 ? go(stats48_kernel<float, false>, a, n, s)
+                              : go(stats48_kernel<bf16_t, false>, a, n, s);
 }
 
 }  // namespace maskgs

@@ -66,6 +66,17 @@ struct BwdArgs {
     Adam adam{};
 };
 
+struct StatsArgs {
+    const float *z;
+    const uint8_t *ref_bits;  // nullable
+    const void *w;            // nullable
+    const float *dz;          // nullable
+    maskgs_stats *stats;
+    float kappa_log2e;        // kappa * log2(e), for max softmax(kappa z)
+    Geometry g;
+    Noise nz;                 // the draw of the sampled hard mask (when sampled)
+};
+
 struct RegArgs {
     const void *w;
     const float *z;
@@ -175,12 +186,14 @@ hipError_t launch_bwd24(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, 
 hipError_t launch_reg24(const RegArgs &a, maskgs_dtype w_dt, hipStream_t s);
 hipError_t launch_hard24(const HardArgs &a, maskgs_dtype w_dt, hipStream_t s);
 hipError_t launch_prior24(const PriorArgs &a, maskgs_dtype w_dt, hipStream_t s);
+hipError_t launch_stats24(const StatsArgs &a, bool sampled, maskgs_dtype w_dt, hipStream_t s);
 
 hipError_t launch_fwd48(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype out_dt, hipStream_t s);
 hipError_t launch_bwd48(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, hipStream_t s);
 hipError_t launch_reg48(const RegArgs &a, maskgs_dtype w_dt, hipStream_t s);
 hipError_t launch_hard48(const HardArgs &a, hipStream_t s);
 hipError_t launch_prior48(const PriorArgs &a, maskgs_dtype w_dt, hipStream_t s);
+hipError_t launch_stats48(const StatsArgs &a, bool sampled, maskgs_dtype w_dt, hipStream_t s);
 
 hipError_t launch_debug_philox(uint64_t seed, uint32_t step, uint32_t tensor_id, uint64_t n0,
                                int64_t count, uint32_t *words, hipStream_t s);

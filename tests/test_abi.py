@@ -126,6 +126,25 @@ def test_bwd_adamw_validation(L):
     assert call(opt(), z=None, m1=None, m2=None, desc=ctypes.byref(e)) == mg.MASKGS_OK
 
 
+def test_mask_stats_validation(L):
+    d = mg.TensorDesc(2, 4, 8, 16, 0, 0)
+    bd = ctypes.byref(d)
+    bad = mg.SampleParams(0, 0, 100.0, 0.0, 0)
+    assert L.maskgs_mask_stats(bd, A, 1.0, None, None, None, 1, None, None, None) == mg.MASKGS_E_NULL
+    assert L.maskgs_mask_stats(bd, None, 1.0, None, None, None, 1, None, A, None) == mg.MASKGS_E_NULL
+    assert L.maskgs_mask_stats(bd, A, -1.0, None, None, None, 1, None, A, None) == mg.MASKGS_E_RANGE
+    assert L.maskgs_mask_stats(bd, A, float("nan"), None, None, None, 1, None, A,
+                               None) == mg.MASKGS_E_RANGE
+    assert L.maskgs_mask_stats(bd, A, 1.0, ctypes.byref(bad), None, None, 1, None, A,
+                               None) == mg.MASKGS_E_RANGE
+    assert L.maskgs_mask_stats(bd, A, 1.0, None, None, A, 9, None, A, None) == mg.MASKGS_E_DTYPE
+    assert L.maskgs_mask_stats(bd, A, 1.0, None, None, None, 1, None, A + 8,
+                               None) == mg.MASKGS_E_ALIGN
+    e = mg.TensorDesc(2, 4, 0, 16, 0, 0)
+    assert L.maskgs_mask_stats(ctypes.byref(e), None, 1.0, None, None, None, 1, None, A,
+                               None) == mg.MASKGS_OK
+
+
 def test_python_wrapper_refuses_cpu_tensors():
     import torch
     t = mg.Tensor(2, 4, 4, 8)
