@@ -11,7 +11,8 @@ pass; that unfused order is timed too and reported beside the step.  Prior
 seeding, an initialisation step, is timed once after the steps.  Then the
 training step with the logit update fused into the backward
 (maskgs_bwd_adamw) is timed with the soft index saved and recomputed, and
-reported under `train_step` (--no-train-step skips it).
+reported under `train_step` (--no-train-step skips it), and one pass of the
+training diagnostics (maskgs_mask_stats) over every tensor under `diagnostics`.
 
 Prints ONE JSON line.  `value` = 2:4 weight blocks per second through the whole
 step; `roofline` describes the kernel with the largest share of the step;
@@ -322,6 +323,30 @@ def main():
                                value=round(total_blocks / (ms_t * 1e-3), 1), kernels=ks)
         del vbufs
 
+    # ---- training diagnostics, one pass over every tensor -----------------
+    # (mask change against the step's hard masks, maximum probability, kept
+    # weight norm against magnitude top-n, logit gradient norm)
+    st = mg.new_stats(dev)
+    stats_bpb = 4 * K + M / 8 + M * wb + 4 * K
+    d0, d1 = ev(), ev()
+    torch.cuda.synchronize()
+    d0.record(stream)
+    for d in bufs:
+        rc = L.maskgs_mask_stats(ctypes.byref(d["desc"]), ptr(d["z"]), ctypes.c_float(wl.kappa),
+                                 None, ptr(d["bits"]), ptr(d["w"]), bf, ptr(d["dz"]), ptr(st),
+                                 sptr)
+        if rc != 0:
+            raise RuntimeError(f"mask_stats: status {rc}")
+    d1.record(stream)
+    torch.cuda.synchronize()
+    stats_ms = d0.elapsed_time(d1)
+    sv = mg.read_stats(st)
+    diagnostics = dict(ms_all_tensors=round(stats_ms, 3), algorithmic_bytes_per_block=stats_bpb,
+                       achieved_gbs=round(stats_bpb * total_blocks / (stats_ms * 1e-3) / 1e9, 1),
+                       changed_fraction=round(sv["changed"] / max(sv["blocks"], 1), 6),
+                       mean_max_prob=round(sv["max_prob"] / max(sv["blocks"], 1), 6),
+                       kept_over_magnitude_l1=round(sv["kept_l1"] / sv["magnitude_l1"], 6))
+
     if args.calibrate_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
@@ -364,6 +389,7 @@ def main():
                                              1)},
         "roofline": roofline,
     }
+    result["diagnostics"] = diagnostics
     if train:
         result["train_step"] = {
             "what": "fwd with the hard mask fused in, then maskgs_bwd_adamw (backward fused with "
