@@ -29,6 +29,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 NO_NOISE = 1
 EXACT_LOGITS = 2
+HARD_SAMPLE = 4
 
 _lib = None
 

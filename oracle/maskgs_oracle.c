@@ -34,6 +34,7 @@
 
 #define ORC_NO_NOISE 1u        /* g = 0 for every candidate (test flag)          */
 #define ORC_EXACT_LOGITS 2u    /* a_i in fp64 instead of the fp32 logit step     */
+#define ORC_HARD_SAMPLE 4u     /* hard Gumbel-max sample, straight-through grad  */
 #define ORC_MAX_K 70           /* C(8,4): the largest candidate set for M <= 8   */
 
 /* ------------------------------------------------------------------------- */
@@ -254,6 +255,18 @@ static void orc_logits(const orc_ctx *c, int64_t b, const float *zb, double *a) 
     }
 }
 
+/* Hard Gumbel-max sample of block b (section 3.4, Eq. 5: the argmax of the
+ * perturbed logits is a draw from softmax(kappa*z)): the first index of the
+ * largest a_i (strict ">" scan), written as the 0/1 mask S_k. */
+static void orc_hard_sample(const orc_ctx *c, int64_t b, const float *zb, double *mk) {
+    double a[ORC_MAX_K];
+    orc_logits(c, b, zb, a);
+    int best = 0;
+    for (int i = 1; i < c->k; ++i)
+        if (a[i] > a[best]) best = i;
+    for (int j = 0; j < c->m; ++j) mk[j] = (c->cand[best] >> j) & 1u ? 1.0 : 0.0;
+}
+
 static void orc_soft_index(const orc_ctx *c, int64_t b, const float *zb, double *y) {
     double a[ORC_MAX_K] = {0.0};
     orc_logits(c, b, zb, a);
@@ -316,6 +329,8 @@ int orc_fwd(int n, int m, int64_t rows, int64_t cols, uint64_t block_offset, uin
         double y[ORC_MAX_K], mk[8];
         orc_soft_index(&c, b, z + b * c.k, y);
         orc_soft_mask(&c, y, mk);
+        /* hard sample: the forward applies S_k (the soft index is still kept) */
+        if (c.flags & ORC_HARD_SAMPLE) orc_hard_sample(&c, b, z + b * c.k, mk);
         for (int j = 0; j < c.m; ++j) {
             double u = (double)w[b * c.m + j] * mk[j];
             if (out_bf16) out_bf16[b * c.m + j] = orc_bf16_from_double(u);
@@ -354,6 +369,9 @@ int orc_bwd(int n, int m, int64_t rows, int64_t cols, uint64_t block_offset, uin
         double y[ORC_MAX_K], mk[8], dm[8], dy[ORC_MAX_K];
         orc_soft_index(&c, b, z + b * c.k, y);
         orc_soft_mask(&c, y, mk);
+        /* straight-through: the regulariser term is that of the mask the
+         * forward applied (S_k); the Jacobian below is the soft index's */
+        if (c.flags & ORC_HARD_SAMPLE) orc_hard_sample(&c, b, z + b * c.k, mk);
         for (int j = 0; j < c.m; ++j) {
             double wj = (double)w[b * c.m + j];
             dm[j] = (double)gup[b * c.m + j] * wj - 2.0 * lambda * wj * wj * mk[j];

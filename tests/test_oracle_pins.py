@@ -693,3 +693,59 @@ def test_mask_change_between_steps_follows_kappa(orc):
         frac = st["changed"] / B
         sd = math.sqrt(expect * (1 - expect) / B) + 1e-12
         assert abs(frac - expect) <= 5 * sd + (0.002 if expect == 0 else 0), (kappa, frac)
+
+
+# --------------------------------------------------------------------------
+# Hard Gumbel-max sample with a straight-through gradient (section 3.4,
+# Eq. 5 Gumbel-max; the hard/soft variants of the Gumbel-softmax)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("nm", [(2, 4), (4, 8)])
+def test_hard_sample_frequencies(orc, nm):
+    """Every block gets the same logits and its own noise: the applied hard
+    masks are Gumbel-max draws, whose frequencies match softmax(kappa*pi) at
+    any temperature (chi^2)."""
+    from scipy import stats
+    n, m = nm
+    K = math.comb(m, n)
+    rng = np.random.default_rng(78)
+    zrow = rng.normal(0, 1.0, size=K).astype(np.float32)
+    blocks = 120000 if K == 6 else 140000
+    rows = blocks // 1000
+    z = np.tile(zrow, (rows * 1000, 1))
+    w = np.ones((rows, m * 1000), dtype=np.float32)
+    r = orc.fwd(n, m, w, z, kappa=1.0, tau=3.0, seed=98, step=5, flags=orc.HARD_SAMPLE,
+                out_dtype="f32")
+    cands = orc.candidates(n, m)
+    got = ((r["out"].reshape(-1, m) != 0) * (1 << np.arange(m))).sum(1)
+    index = {int(c): i for i, c in enumerate(cands)}
+    counts = np.bincount([index[int(g)] for g in got], minlength=K)
+    p = np.exp(zrow.astype(np.float64) - zrow.max())
+    p /= p.sum()
+    chi2 = ((counts - blocks * p) ** 2 / (blocks * p)).sum()
+    assert chi2 < stats.chi2.ppf(1 - 1e-6, K - 1)
+
+
+@pytest.mark.parametrize("nm", [(2, 4), (4, 8)])
+def test_hard_sample_forward_and_straight_through(orc, nm):
+    n, m = nm
+    w, z, G = _rand_inputs(16, 8 * m, n, m, seed=24)
+    kw = dict(kappa=100.0, tau=2.0, seed=3, step=1, tensor_id=5, block_offset=9)
+    soft = orc.fwd(n, m, w, z, out_dtype="f32", **kw)
+    hard = orc.fwd(n, m, w, z, out_dtype="f32", flags=orc.HARD_SAMPLE, **kw)
+    # the soft index is unchanged; the applied mask keeps exactly N weights of a
+    # valid candidate, bit for bit, and R is the sum of their squares
+    assert np.array_equal(soft["y"], hard["y"])
+    ob = hard["out"].reshape(-1, m)
+    wb = w.reshape(-1, m)
+    kept = ob != 0
+    assert (kept.sum(1) == n).all() and np.array_equal(ob[kept], wb[kept])
+    cands = set(int(c) for c in orc.candidates(n, m))
+    assert all(int(k) in cands for k in (kept * (1 << np.arange(m))).sum(1))
+    assert abs(hard["reg"] - float((wb[kept].astype(np.float64) ** 2).sum())) <= 1e-12 * hard["reg"]
+    # straight-through: only the regulariser term sees the hard mask
+    d_soft = orc.bwd(n, m, w, z, G, lam=0.0, **kw)
+    d_hard = orc.bwd(n, m, w, z, G, lam=0.0, flags=orc.HARD_SAMPLE, **kw)
+    assert np.array_equal(d_soft, d_hard)
+    d_hard = orc.bwd(n, m, w, z, G, lam=0.5, flags=orc.HARD_SAMPLE, **kw)
+    assert not np.array_equal(d_hard, orc.bwd(n, m, w, z, G, lam=0.5, **kw))
+    assert np.abs(d_hard.sum(axis=1)).max() <= 1e-12 * np.abs(d_hard).max()  # sum_i dz_i = 0
