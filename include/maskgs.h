@@ -60,6 +60,13 @@ typedef enum { MASKGS_F32 = 0, MASKGS_BF16 = 1 } maskgs_dtype;
 
 /* Sample flags. */
 #define MASKGS_NO_NOISE 1u /* g = 0 for every candidate (tests and diagnostics) */
+/* Hard Gumbel-max sample with a straight-through gradient (section 3.4, Eq. 5:
+ * the first argmax k of the perturbed logits a is a draw from softmax(kappa z)).
+ * Forward: W (.) S_k and its regulariser instead of W (.) M~; the soft index y
+ * is still computed and saved.  Backward: the softmax Jacobian of y, with the
+ * regulariser term taken at S_k.  The backward needs k, so it recomputes y
+ * from z: with a saved y it returns MASKGS_E_UNSUPPORTED. */
+#define MASKGS_HARD_SAMPLE 2u
 
 /* One weight tensor (or a row range of one).  block_offset is the global index
  * of the first block described: the noise of a block depends on its global

@@ -32,6 +32,7 @@ MASKGS_E_CAPACITY = 8
 MASKGS_F32 = 0
 MASKGS_BF16 = 1
 MASKGS_NO_NOISE = 1
+MASKGS_HARD_SAMPLE = 2
 
 EXPORTS = ("maskgs_abi_version", "maskgs_status_str", "maskgs_candidates", "maskgs_fwd",
            "maskgs_fwd_hard",

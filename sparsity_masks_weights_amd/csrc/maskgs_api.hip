@@ -70,6 +70,7 @@ int check_params(const maskgs_sample_params *p, Noise *nz) {
     nz->tau_inv = tau_inv;
     nz->grad_scale = static_cast<double>(p->kappa) / static_cast<double>(p->tau);
     nz->no_noise = (p->flags & MASKGS_NO_NOISE) ? 1u : 0u;
+    nz->hard_sample = (p->flags & MASKGS_HARD_SAMPLE) ? 1u : 0u;
     return MASKGS_OK;
 }
 
@@ -166,6 +167,7 @@ int maskgs_bwd(const maskgs_tensor_desc *t, const maskgs_sample_params *p, const
     if ((rc = check_params(p, &nz))) return rc;
     if (!std::isfinite(lambda) || lambda < 0.0f) return MASKGS_E_RANGE;
     if (g.nblocks == 0) return MASKGS_OK;
+    if (nz.hard_sample && y_saved) return MASKGS_E_UNSUPPORTED;
     if (!w || !dout || !dz || (!z && !y_saved)) return MASKGS_E_NULL;
     if (!valid_dtype(w_dt) || !valid_dtype(dout_dt)) return MASKGS_E_DTYPE;
     if (misaligned(w) || misaligned(z) || misaligned(y_saved) || misaligned(dout) ||
@@ -194,6 +196,7 @@ int maskgs_bwd_adamw(const maskgs_tensor_desc *t, const maskgs_sample_params *p,
         !(opt->beta2 >= 0.0f && opt->beta2 < 1.0f) || !(opt->eps > 0.0f) ||
         opt->weight_decay < 0.0f || opt->t == 0)
         return MASKGS_E_RANGE;
+    if (nz.hard_sample && y_saved) return MASKGS_E_UNSUPPORTED;
     if (g.nblocks == 0) return MASKGS_OK;
     if (!w || !dout || !z || !exp_avg || !exp_avg_sq) return MASKGS_E_NULL;
     if (!valid_dtype(w_dt) || !valid_dtype(dout_dt)) return MASKGS_E_DTYPE;
@@ -250,6 +253,7 @@ int maskgs_reg_reduce(const maskgs_tensor_desc *t, const maskgs_sample_params *p
     if (rc) return rc;
     if ((rc = check_params(p, &nz))) return rc;
     if (g.nblocks == 0) return MASKGS_OK;
+    if (nz.hard_sample && y_saved) return MASKGS_E_UNSUPPORTED;
     if (!w || !reg_accum || (!z && !y_saved)) return MASKGS_E_NULL;
     if (!valid_dtype(w_dt)) return MASKGS_E_DTYPE;
     if (misaligned(w) || misaligned(z) || misaligned(y_saved) || misaligned(reg_accum))

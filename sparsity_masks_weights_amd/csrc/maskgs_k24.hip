@@ -319,13 +319,33 @@ __device__ __forceinline__ void pair_logits(const Geometry &g, const Noise &nz, 
     }
 }
 
+// Soft index of a pair and, under the hard-sample flag, the masks of its two
+// Gumbel-max samples S[first argmax a] (0 otherwise).
 template <int PHASE>
-__device__ __forceinline__ void pair_soft_index(const FwdArgs &a, int64_t p, const float (&z)[12],
-                                                float (&y)[12]) {
+__device__ __forceinline__ void pair_sample(const Geometry &g, const Noise &nz, int64_t p,
+                                            const float (&z)[12], float (&y)[12],
+                                            uint32_t (&hm)[2]) {
     float a12[12];
-    pair_logits<PHASE>(a.g, a.nz, p, z, a12);
+    pair_logits<PHASE>(g, nz, p, z, a12);
+    hm[0] = hm[1] = 0u;
+    if (nz.hard_sample) {
+        hm[0] = cand_mask6(first_argmax6(a12));
+        hm[1] = cand_mask6(first_argmax6(a12 + 6));
+    }
     softmax6(a12, y);
     softmax6(a12 + 6, y + 6);
+}
+
+// The mask the forward applies to a block: the soft mask y.S (Eq. 7), or the
+// hard sample's 0/1 mask.
+__device__ __forceinline__ void applied_mask4(const float *y6, uint32_t hm, bool hard,
+                                              float (&m)[4]) {
+    if (hard) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m[j] = ((hm >> j) & 1u) ? 1.0f : 0.0f;
+    } else {
+        soft_mask4(y6, m);
+    }
 }
 
 // Workgroup sum of one double per lane, added atomically to *dst.
@@ -370,12 +390,13 @@ __global__ __launch_bounds__(kThreads) void fwd24_kernel(FwdArgs a) {
                 for (int j = 0; j < 8; ++j) r[j] = Io<WT>::raw_of(w[j]);
                 hard_pair<WT>(a.idx, a.bits, a.values, a.val_idx, p, two, z, r);
             }
-            pair_soft_index<PHASE>(a, p, z, y);
+            uint32_t hm[2];
+            pair_sample<PHASE>(a.g, a.nz, p, z, y, hm);
             float racc = 0.0f;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 float m[4];
-                soft_mask4(y + 6 * h, m);
+                applied_mask4(y + 6 * h, hm[h], a.nz.hard_sample, m);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const float u = w[4 * h + j] * m[j];
@@ -409,6 +430,7 @@ __global__ __launch_bounds__(kThreads) void bwd24_kernel(BwdArgs a) {
         if (p < npairs) {
             const bool two = 2 * p + 1 < a.g.nblocks;
             float w[8], G[8], y[12];
+            uint32_t hm[2] = {0u, 0u};
             Io<WT>::load8(a.w, p, two, w);
             Io<GT>::load8(a.dout, p, two, G);
             if (SAVED) {
@@ -416,15 +438,16 @@ __global__ __launch_bounds__(kThreads) void bwd24_kernel(BwdArgs a) {
             } else {
                 float z[12];
                 load12(a.z, p, two, z);
-                const FwdArgs f{a.w, a.z, nullptr, nullptr, nullptr, a.g, a.nz};
-                pair_soft_index<PHASE>(f, p, z, y);
+                pair_sample<PHASE>(a.g, a.nz, p, z, y, hm);
             }
             float prev[12];
             if (a.accumulate) load12(a.dz, p, two, prev);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
+                // the regulariser term is that of the applied mask (straight-
+                // through under the hard sample); the Jacobian is y's
                 float m[4];
-                soft_mask4(y + 6 * h, m);
+                applied_mask4(y + 6 * h, hm[h], !SAVED && a.nz.hard_sample, m);
                 double dm[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -486,20 +509,20 @@ __global__ __launch_bounds__(kThreads) void reg24_kernel(RegArgs a) {
          p += stride) {
         const bool two = 2 * p + 1 < a.g.nblocks;
         float w[8], y[12];
+        uint32_t hm[2] = {0u, 0u};
         Io<WT>::load8(a.w, p, two, w);
         if (SAVED) {
             load12(a.y, p, two, y);
         } else {
             float z[12];
             load12(a.z, p, two, z);
-            const FwdArgs f{a.w, a.z, nullptr, nullptr, nullptr, a.g, a.nz};
-            pair_soft_index<PHASE>(f, p, z, y);
+            pair_sample<PHASE>(a.g, a.nz, p, z, y, hm);
         }
         float racc = 0.0f;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             float m[4];
-            soft_mask4(y + 6 * h, m);
+            applied_mask4(y + 6 * h, hm[h], !SAVED && a.nz.hard_sample, m);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float u = w[4 * h + j] * m[j];

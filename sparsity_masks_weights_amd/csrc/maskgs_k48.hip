@@ -269,20 +269,33 @@ __device__ __forceinline__ void logits70(float (&v)[kK], uint64_t gb, const Geom
 }
 
 // In place: a -> y = softmax(a) (Eq. 6).  Exponentials scaled by 2^64 so that
-// small soft-index values are rounded correctly instead of flushed.
-__device__ __forceinline__ void softmax70(float (&v)[kK]) {
+// small soft-index values are rounded correctly instead of flushed.  With
+// SAMPLE, also returns the mask of the hard Gumbel-max sample, the candidate
+// of the first largest a_i: a_i - amax is +0 or -0 exactly there (the same
+// ordered key as argmax_key70, taken in the exponential's loop).
+template <bool SAMPLE = false>
+__device__ __forceinline__ void softmax70(float (&v)[kK], uint32_t *hard_mask = nullptr) {
     float amax = v[0];
 #pragma unroll
     for (int i = 1; i < kK; ++i) amax = fmaxf(amax, v[i]);
     float s = 0.0f;
+    uint32_t best = 0xFFFFFFFFu;
 #pragma unroll
     for (int i = 0; i < kK; ++i) {
-        v[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i] - amax, 1.44269504088896341f, 64.0f));
+        const float d = v[i] - amax;
+        if (SAMPLE) {
+            const uint32_t nz = __float_as_uint(d) << 1;  // 0 iff a_i is the maximum
+            const uint32_t key = ((nz < 1u ? nz : 1u) << 15) | (static_cast<uint32_t>(i) << 8) |
+                                 C48::at(i);
+            best = best < key ? best : key;
+        }
+        v[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(d, 1.44269504088896341f, 64.0f));
         s += v[i];
     }
     const float inv = __builtin_amdgcn_rcpf(s);
 #pragma unroll
     for (int i = 0; i < kK; ++i) v[i] *= inv;
+    if (SAMPLE) *hard_mask = best & 0xFFu;
 }
 
 // Soft mask m_j = sum_i y_i S_ij (Eq. 7), candidates in table order.
@@ -318,6 +331,17 @@ __device__ __forceinline__ uint32_t argmax_key70(const Src &v) {
     return best & 0x7FFFu;
 }
 
+// The mask the forward applies: the soft mask y.S (Eq. 7) or the hard sample.
+__device__ __forceinline__ void applied_mask8(const float (&y)[kK], uint32_t hm, bool hard,
+                                              float (&m)[8]) {
+    if (hard) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m[j] = ((hm >> j) & 1u) ? 1.0f : 0.0f;
+    } else {
+        soft_mask8(y, m);
+    }
+}
+
 __device__ __forceinline__ void reduce_add_wave(double v, double *dst) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
@@ -331,7 +355,7 @@ __device__ __forceinline__ int64_t tile_count(int64_t nblocks) {
 // ---------------------------------------------------------------------------
 // Forward (noise kernel, registers).
 // ---------------------------------------------------------------------------
-template <typename WT, typename OT, bool HARD>
+template <typename WT, typename OT, bool HARD, bool SAMPLE>
 __global__ __launch_bounds__(kWave) void fwd48_kernel(FwdArgs a) {
     __shared__ float4 stage4[kHalf * kK / 4];
     float *stage = reinterpret_cast<float *>(stage4);
@@ -352,9 +376,10 @@ __global__ __launch_bounds__(kWave) void fwd48_kernel(FwdArgs a) {
                 if (a.bits) a.bits[b] = static_cast<uint8_t>(key);
             }
             logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz);
-            softmax70(v);
+            uint32_t hm = 0u;
+            softmax70<SAMPLE>(v, &hm);
             float m[8], w[8], out[8];
-            soft_mask8(v, m);
+            applied_mask8(v, hm, SAMPLE, m);
             Io8<WT>::load(a.w, b, w);
             float racc = 0.0f;
 #pragma unroll
@@ -373,7 +398,7 @@ __global__ __launch_bounds__(kWave) void fwd48_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // Regulariser value (section 3.4, Eq. 8), recomputing the soft index.
 // ---------------------------------------------------------------------------
-template <typename WT>
+template <typename WT, bool SAMPLE>
 __global__ __launch_bounds__(kWave) void reg48_noise_kernel(RegArgs a) {
     __shared__ float4 stage4[kHalf * kK / 4];
     float *stage = reinterpret_cast<float *>(stage4);
@@ -388,9 +413,10 @@ __global__ __launch_bounds__(kWave) void reg48_noise_kernel(RegArgs a) {
         tile_in<false>(a.z, b0, nb, stage, v);
         if (lane < nb) {
             logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz);
-            softmax70(v);
+            uint32_t hm = 0u;
+            softmax70<SAMPLE>(v, &hm);
             float m[8], w[8];
-            soft_mask8(v, m);
+            applied_mask8(v, hm, SAMPLE, m);
             Io8<WT>::load(a.w, b, w);
             float racc = 0.0f;
 #pragma unroll
@@ -454,7 +480,7 @@ __device__ __forceinline__ void row_soft_mask_f64(const float *row, double (&md)
 // dm_j = G_j w_j - 2 lambda w_j (w_j m_j); sum_i y_i dy_i = sum_j m_j dm_j;
 // dz_i = (kappa/tau) y_i (dy_i - s), dy_i = sum_{j in S_i} dm_j, with
 // s = sum_i y_i dy_i / sum_i y_i.
-template <typename WT, typename GT, bool SAVED, bool ACC, bool ADAMW>
+template <typename WT, typename GT, bool SAVED, bool ACC, bool ADAMW, bool SAMPLE>
 __global__ __launch_bounds__(kWave) void bwd48_kernel(BwdArgs a) {
     __shared__ float4 tile4[kWave * kK / 4];
     __shared__ float4 prev4[ACC ? kWave * kK / 4 : 1];
@@ -480,12 +506,13 @@ __global__ __launch_bounds__(kWave) void bwd48_kernel(BwdArgs a) {
         __syncthreads();
         float *row = tl + lane * kK;
         if (lane < nb) {
+            uint32_t hm = 0u;
             if (!SAVED) {
                 float v[kK];
 #pragma unroll
                 for (int i = 0; i < kK; ++i) v[i] = row[i];
                 logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz);
-                softmax70(v);
+                softmax70<SAMPLE>(v, &hm);
 #pragma unroll
                 for (int i = 0; i < kK; ++i) row[i] = v[i];
                 row_pass_barrier();
@@ -493,8 +520,12 @@ __global__ __launch_bounds__(kWave) void bwd48_kernel(BwdArgs a) {
             float m[8];
             double md[8], dm[8];
             row_soft_mask_f64(row, md);
+            // the regulariser term is that of the applied mask (straight-through
+            // under the hard sample); the Jacobian below is y's
+            const bool hard = !SAVED && SAMPLE;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) m[j] = static_cast<float>(md[j]);
+            for (int j = 0; j < 8; ++j)
+                m[j] = hard ? (((hm >> j) & 1u) ? 1.0f : 0.0f) : static_cast<float>(md[j]);
             // s = sum_i y_i dy_i / sum_i y_i = sum_j m_j dm_j / (sum_j m_j / 4): the
             // division by the actual sum of the fp32 soft index keeps dy_i - s
             // free of the fp32 rounding of y (see the 2:4 backward)
@@ -774,47 +805,61 @@ hipError_t go(Kern kernel, const A &args, int64_t nblocks, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_fwd48(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype out_dt, hipStream_t s) {
+template <bool HARD, bool SAMPLE>
+hipError_t fwd48_dispatch(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype out_dt, hipStream_t s) {
     const int64_t n = a.g.nblocks;
-    if (a.idx || a.bits) {
-        if (w_dt == MASKGS_BF16 && out_dt == MASKGS_BF16)
-            return go(fwd48_kernel<bf16_t, bf16_t, true>, a, n, s);
-        if (w_dt == MASKGS_BF16) return go(fwd48_kernel<bf16_t, float, true>, a, n, s);
-        if (out_dt == MASKGS_BF16) return go(fwd48_kernel<float, bf16_t, true>, a, n, s);
-        return go(fwd48_kernel<float, float, true>, a, n, s);
-    }
     if (w_dt == MASKGS_BF16 && out_dt == MASKGS_BF16)
-        return go(fwd48_kernel<bf16_t, bf16_t, false>, a, n, s);
-    if (w_dt == MASKGS_BF16) return go(fwd48_kernel<bf16_t, float, false>, a, n, s);
-    if (out_dt == MASKGS_BF16) return go(fwd48_kernel<float, bf16_t, false>, a, n, s);
-    return go(fwd48_kernel<float, float, false>, a, n, s);
+        return go(fwd48_kernel<bf16_t, bf16_t, HARD, SAMPLE>, a, n, s);
+    if (w_dt == MASKGS_BF16) return go(fwd48_kernel<bf16_t, float, HARD, SAMPLE>, a, n, s);
+    if (out_dt == MASKGS_BF16) return go(fwd48_kernel<float, bf16_t, HARD, SAMPLE>, a, n, s);
+    return go(fwd48_kernel<float, float, HARD, SAMPLE>, a, n, s);
 }
 
-template <bool SAVED, bool ACC, bool ADAMW>
+hipError_t launch_fwd48(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype out_dt, hipStream_t s) {
+    const bool hard = a.idx || a.bits;
+    if (a.nz.hard_sample)
+        return hard ? fwd48_dispatch<true, true>(a, w_dt, out_dt, s)
+                    : fwd48_dispatch<false, true>(a, w_dt, out_dt, s);
+    return hard ? fwd48_dispatch<true, false>(a, w_dt, out_dt, s)
+                : fwd48_dispatch<false, false>(a, w_dt, out_dt, s);
+}
+
+template <bool SAVED, bool ACC, bool ADAMW, bool SAMPLE>
 hipError_t bwd48_dispatch(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, hipStream_t s) {
     const int64_t n = a.g.nblocks;
     const bool wb = w_dt == MASKGS_BF16, gb = g_dt == MASKGS_BF16;
-    if (wb && gb) return go(bwd48_kernel<bf16_t, bf16_t, SAVED, ACC, ADAMW>, a, n, s);
-    if (wb) return go(bwd48_kernel<bf16_t, float, SAVED, ACC, ADAMW>, a, n, s);
-    if (gb) return go(bwd48_kernel<float, bf16_t, SAVED, ACC, ADAMW>, a, n, s);
-    return go(bwd48_kernel<float, float, SAVED, ACC, ADAMW>, a, n, s);
+    if (wb && gb) return go(bwd48_kernel<bf16_t, bf16_t, SAVED, ACC, ADAMW, SAMPLE>, a, n, s);
+    if (wb) return go(bwd48_kernel<bf16_t, float, SAVED, ACC, ADAMW, SAMPLE>, a, n, s);
+    if (gb) return go(bwd48_kernel<float, bf16_t, SAVED, ACC, ADAMW, SAMPLE>, a, n, s);
+    return go(bwd48_kernel<float, float, SAVED, ACC, ADAMW, SAMPLE>, a, n, s);
 }
 
 hipError_t launch_bwd48(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, hipStream_t s) {
-    if (a.m1)  // fused AdamW update (never with accumulation)
-        return a.y ? bwd48_dispatch<true, false, true>(a, w_dt, g_dt, s)
-                   : bwd48_dispatch<false, false, true>(a, w_dt, g_dt, s);
-    if (a.y) return a.accumulate ? bwd48_dispatch<true, true, false>(a, w_dt, g_dt, s)
-                                 : bwd48_dispatch<true, false, false>(a, w_dt, g_dt, s);
-    return a.accumulate ? bwd48_dispatch<false, true, false>(a, w_dt, g_dt, s)
-                        : bwd48_dispatch<false, false, false>(a, w_dt, g_dt, s);
+    // the hard sample comes with a recomputed soft index only (checked by the API)
+    const bool smp = a.nz.hard_sample && !a.y;
+    if (a.m1) {  // fused AdamW update (never with accumulation)
+        if (a.y) return bwd48_dispatch<true, false, true, false>(a, w_dt, g_dt, s);
+        return smp ? bwd48_dispatch<false, false, true, true>(a, w_dt, g_dt, s)
+                   : bwd48_dispatch<false, false, true, false>(a, w_dt, g_dt, s);
+    }
+    if (a.y) return a.accumulate ? bwd48_dispatch<true, true, false, false>(a, w_dt, g_dt, s)
+                                 : bwd48_dispatch<true, false, false, false>(a, w_dt, g_dt, s);
+    if (smp)
+        return a.accumulate ? bwd48_dispatch<false, true, false, true>(a, w_dt, g_dt, s)
+                            : bwd48_dispatch<false, false, false, true>(a, w_dt, g_dt, s);
+    return a.accumulate ? bwd48_dispatch<false, true, false, false>(a, w_dt, g_dt, s)
+                        : bwd48_dispatch<false, false, false, false>(a, w_dt, g_dt, s);
 }
 
 hipError_t launch_reg48(const RegArgs &a, maskgs_dtype w_dt, hipStream_t s) {
     const int64_t n = a.g.nblocks;
-    if (w_dt == MASKGS_BF16)
-        return a.y ? go(reg48_saved_kernel<bf16_t>, a, n, s) : go(reg48_noise_kernel<bf16_t>, a, n, s);
-    return a.y ? go(reg48_saved_kernel<float>, a, n, s) : go(reg48_noise_kernel<float>, a, n, s);
+    const bool bf = w_dt == MASKGS_BF16;
+    if (a.y) return bf ? go(reg48_saved_kernel<bf16_t>, a, n, s) : go(reg48_saved_kernel<float>, a, n, s);
+    if (a.nz.hard_sample)
+        return bf ? go(reg48_noise_kernel<bf16_t, true>, a, n, s)
+                  : go(reg48_noise_kernel<float, true>, a, n, s);
+    return bf ? go(reg48_noise_kernel<bf16_t, false>, a, n, s)
+              : go(reg48_noise_kernel<float, false>, a, n, s);
 }
 
 hipError_t launch_hard48(const HardArgs &a, hipStream_t s) {

@@ -25,6 +25,7 @@ struct Noise {
     float kappa, tau_inv;
     double grad_scale;
     uint32_t no_noise;
+    uint32_t hard_sample;  // apply S[first argmax a] (straight-through backward)
 };
 
 struct FwdArgs {

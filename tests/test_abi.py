@@ -145,6 +145,17 @@ def test_mask_stats_validation(L):
                                None) == mg.MASKGS_OK
 
 
+def test_hard_sample_needs_recomputed_soft_index(L):
+    d = mg.TensorDesc(2, 4, 8, 16, 0, 0)
+    p = mg.SampleParams(0, 0, 100.0, 4.0, mg.MASKGS_HARD_SAMPLE)
+    bd, bp = ctypes.byref(d), ctypes.byref(p)
+    assert L.maskgs_bwd(bd, bp, A, 1, A, A, A, 1, 1e-5, A, 0, None) == mg.MASKGS_E_UNSUPPORTED
+    assert L.maskgs_reg_reduce(bd, bp, A, 1, A, A, A, None) == mg.MASKGS_E_UNSUPPORTED
+    opt = mg.AdamWParams(5e-4, 0.9, 0.999, 1e-8, 0.1, 1)
+    assert L.maskgs_bwd_adamw(bd, bp, A, 1, A, A, A, 1, 1e-5, A, A, ctypes.byref(opt),
+                              None) == mg.MASKGS_E_UNSUPPORTED
+
+
 def test_python_wrapper_refuses_cpu_tensors():
     import torch
     t = mg.Tensor(2, 4, 4, 8)
