@@ -12,7 +12,9 @@ seeding, an initialisation step, is timed once after the steps.  Then the
 training step with the logit update fused into the backward
 (maskgs_bwd_adamw) is timed with the soft index saved and recomputed, and
 reported under `train_step` (--no-train-step skips it), and one pass of the
-training diagnostics (maskgs_mask_stats) over every tensor under `diagnostics`.
+training diagnostics (maskgs_mask_stats) over every tensor under `diagnostics`,
+and the step with the hard Gumbel-max sample (straight-through backward) under
+`hard_sample_step`.
 
 Prints ONE JSON line.  `value` = 2:4 weight blocks per second through the whole
 step; `roofline` describes the kernel with the largest share of the step;
@@ -347,6 +349,51 @@ def main():
                        mean_max_prob=round(sv["max_prob"] / max(sv["blocks"], 1), 6),
                        kept_over_magnitude_l1=round(sv["kept_l1"] / sv["magnitude_l1"], 6))
 
+    # ---- hard Gumbel-max sample, straight-through backward ----------------
+    # (forward with the hard mask of the same logits, soft index recomputed in
+    # the backward, which needs the sample)
+    hs_params = mg.SampleParams(0, 0, wl.kappa, wl.tau, mg.MASKGS_HARD_SAMPLE)
+    hsref = ctypes.byref(hs_params)
+    hs = {"fwd_hard": [], "bwd": []}
+    h0, h1 = ev(), ev()
+    torch.cuda.synchronize()
+    h0.record(stream)
+    for s_ in range(args.steps):
+        hs_params.step = s_
+        reg.zero_()
+        for kind in ("fwd_hard", "bwd"):
+            p0, p1 = ev(), ev()
+            p0.record(stream)
+            for d in bufs:
+                dref = ctypes.byref(d["desc"])
+                if kind == "fwd_hard":
+                    rc = L.maskgs_fwd_hard(dref, hsref, ptr(d["w"]), bf, ptr(d["z"]), ptr(d["out"]),
+                                           bf, None, ptr(reg), None, ptr(d["bits"]),
+                                           ptr(d["vals"]), ptr(d["vidx"]), sptr)
+                else:
+                    rc = L.maskgs_bwd(dref, hsref, ptr(d["w"]), bf, ptr(d["z"]), None, ptr(d["G"]),
+                                      gdt, ctypes.c_float(wl.lam), ptr(d["dz"]), 0, sptr)
+                if rc != 0:
+                    raise RuntimeError(f"hard sample {kind}: status {rc}")
+            p1.record(stream)
+            hs[kind].append((p0, p1))
+    h1.record(stream)
+    torch.cuda.synchronize()
+    ms_hs = h0.elapsed_time(h1) / args.steps
+    hs_bytes = {"fwd_hard": per_block_bytes["fwd_hard"] - 4 * K,
+                "bwd": M * wb + M * gb + 4 * K + 4 * K}
+    hard_sample_step = dict(
+        what="MASKGS_HARD_SAMPLE: forward applying the Gumbel-max sample (hard mask of the "
+             "same logits fused in, soft index not saved), straight-through backward "
+             "recomputing the soft index",
+        ms_per_step=round(ms_hs, 3), value=round(total_blocks / (ms_hs * 1e-3), 1),
+        kernels={k: dict(ms_per_step=round(sum(a.elapsed_time(b) for a, b in v) / args.steps, 4),
+                         algorithmic_bytes_per_block=hs_bytes[k],
+                         achieved_gbs=round(hs_bytes[k] * total_blocks /
+                                            (sum(a.elapsed_time(b) for a, b in v) / args.steps
+                                             * 1e-3) / 1e9, 1))
+                 for k, v in hs.items()})
+
     if args.calibrate_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
@@ -390,6 +437,7 @@ def main():
         "roofline": roofline,
     }
     result["diagnostics"] = diagnostics
+    result["hard_sample_step"] = hard_sample_step
     if train:
         result["train_step"] = {
             "what": "fwd with the hard mask fused in, then maskgs_bwd_adamw (backward fused with "
