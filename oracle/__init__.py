@@ -11,6 +11,11 @@ marshals numpy arrays into it.  Every function cites the passage of the MaskLLM
 summary page ("MaskLLM: Learnable Semi-Structured Sparsity for Large Language
 Models", paper-graph-ui summary of arXiv 2409.17481) that it follows.
 
+``maskpro_oracle.c`` (built into the same library) holds the linear-space
+variant MaskPro ("MaskPro: Linear-Space Probabilistic Learning for Strict
+(N:M)-Sparsity on LLMs", atlas.scime.ai summary page); its functions are the
+``maskpro_*`` ones below and its readings are listed in that file's header.
+
 Parity pins of this oracle live in ``tests/test_oracle_*.py``.  Parity unpinned
 (self-consistent definitions the pages do not fix): the choice of Philox word
 layout, of the uniform map and of the contract logarithm's coefficients.
@@ -25,6 +30,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "maskgs_oracle.c")
+_SRC_MP = os.path.join(_HERE, "maskpro_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 NO_NOISE = 1
@@ -38,7 +44,7 @@ def build() -> str:
     """Compile the oracle with gcc (always recompiles).  Returns the .so path."""
     tmp = _LIB + ".tmp"
     cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-shared",
-           "-fPIC", "-std=c11", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+           "-fPIC", "-std=c11", "-Wall", "-Wextra", "-o", tmp, _SRC, _SRC_MP, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)
     return _LIB
@@ -89,6 +95,18 @@ def lib():
     L.orc_prior_init.argtypes = [c.c_int, c.c_int, c.c_int64, c.c_int64, P, P, P,
                                  c.c_float, c.c_int]
     L.orc_prior_init.restype = c.c_int
+    mp = [c.c_int, c.c_int, c.c_int64, c.c_int64, c.c_uint64, c.c_uint32, c.c_uint64,
+          c.c_uint32, c.c_uint32]
+    L.orc_mp_fwd.argtypes = mp + [P, P, P, P, P, P]
+    L.orc_mp_fwd.restype = c.c_int
+    L.orc_mp_grad.argtypes = mp + [P, P, c.c_double, P, P]
+    L.orc_mp_grad.restype = c.c_int
+    L.orc_mp_logp.argtypes = [c.c_int, c.c_int, c.c_int64, P, P, P]
+    L.orc_mp_logp.restype = c.c_int
+    L.orc_mp_init.argtypes = [c.c_int, c.c_int, c.c_int64, c.c_int64, P, P, c.c_float, P]
+    L.orc_mp_init.restype = c.c_int
+    L.orc_mp_baseline.argtypes = [c.c_int64, P, c.c_double, P, P]
+    L.orc_mp_baseline.restype = c.c_int
     _lib = L
     return L
 
@@ -334,3 +352,86 @@ def prior_init(n, m, z, rows, cols, *, alpha, mode=0, prior_bits=None, w=None):
     if rc != 0:
         raise ValueError(f"oracle prior_init: rc={rc}")
     return zz
+
+
+# --------------------------------------------------------------------------
+# MaskPro (linear-space logits, N-way draw without replacement, policy
+# gradient); arithmetic and readings in maskpro_oracle.c.
+# --------------------------------------------------------------------------
+MP_NO_NOISE = 1
+
+
+def maskpro_fwd(n, m, w, pi, *, seed=0, step=0, tensor_id=0, block_offset=0, flags=0,
+                out_dtype="bf16"):
+    """Ordered draw and masked weight ("Approach": N-way sampling without
+    replacement from one categorical per block of M).
+
+    w: fp32 [rows, cols]; pi: fp32 [B, M].  Returns dict(order=[B, N] uint8
+    positions in draw order, bits=packed LSB-first mask, out=[rows, cols]
+    masked weight (uint16 bf16 bits or fp32))."""
+    w = _f32(w)
+    rows, cols = w.shape
+    B = rows * (cols // m)
+    pi = _f32(pi).reshape(B, m)
+    order = np.zeros((B, n), dtype=np.uint8)
+    bits = np.zeros((B * m + 7) // 8, dtype=np.uint8)
+    out16 = np.zeros((rows, cols), dtype=np.uint16) if out_dtype == "bf16" else None
+    out32 = np.zeros((rows, cols), dtype=np.float32) if out_dtype == "f32" else None
+    rc = lib().orc_mp_fwd(n, m, rows, cols, block_offset, tensor_id, seed, step, flags,
+                          _ptr(w), _ptr(pi), _ptr(order), _ptr(bits), _ptr(out16), _ptr(out32))
+    if rc != 0:
+        raise ValueError("oracle maskpro_fwd: invalid arguments")
+    return dict(order=order, bits=bits, out=out16 if out16 is not None else out32)
+
+
+def maskpro_logp(n, m, pi, order):
+    """log-likelihood of each block's ordered draw, f64 [B]."""
+    pi = _f32(pi).reshape(-1, m)
+    B = pi.shape[0]
+    order = np.ascontiguousarray(order, dtype=np.uint8).reshape(B, n)
+    out = np.zeros(B, dtype=np.float64)
+    if lib().orc_mp_logp(n, m, B, _ptr(pi), _ptr(order), _ptr(out)) != 0:
+        raise ValueError("oracle maskpro_logp: invalid arguments")
+    return out
+
+
+def maskpro_grad(n, m, pi, rows, cols, *, advantage, order=None, seed=0, step=0, tensor_id=0,
+                 block_offset=0, flags=0, dpi_prev=None):
+    """Policy gradient A * d(log p)/d(pi), f64 [B, M]; the draw is `order`
+    ([B, N] positions) or, when None, the draw of maskpro_fwd with the same
+    noise arguments.  dpi_prev: accumulate onto it."""
+    B = rows * (cols // m)
+    pi = _f32(pi).reshape(B, m)
+    od = None if order is None else np.ascontiguousarray(order, dtype=np.uint8).reshape(B, n)
+    prev = None if dpi_prev is None else _f32(dpi_prev).reshape(B, m)
+    out = np.zeros((B, m), dtype=np.float64)
+    rc = lib().orc_mp_grad(n, m, rows, cols, block_offset, tensor_id, seed, step, flags,
+                           _ptr(pi), _ptr(od), float(advantage), _ptr(prev), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle maskpro_grad: invalid arguments")
+    return out
+
+
+def maskpro_init(n, m, rows, cols, *, c, prior_bits=None, w=None):
+    """Initial logits: C at the initial mask's kept positions, 0 elsewhere;
+    fp32 [B, M].  The mask is prior_bits (packed) or the magnitude top-N of w."""
+    B = rows * (cols // m)
+    pb = None if prior_bits is None else np.ascontiguousarray(prior_bits, dtype=np.uint8)
+    ww = None if w is None else _f32(w)
+    if pb is None and ww is None:
+        raise ValueError("maskpro_init needs prior_bits or w")
+    pi = np.zeros((B, m), dtype=np.float32)
+    if lib().orc_mp_init(n, m, rows, cols, _ptr(pb), _ptr(ww), float(c), _ptr(pi)) != 0:
+        raise ValueError("oracle maskpro_init: invalid arguments")
+    return pi
+
+
+def maskpro_baseline(residuals, *, mu, b0=0.0):
+    """Advantages of a sequence of loss residuals under the moving-average
+    baseline; returns (adv [T] f64, baseline after the last step)."""
+    r = np.ascontiguousarray(residuals, dtype=np.float64)
+    adv = np.zeros(len(r), dtype=np.float64)
+    b = ctypes.c_double(float(b0))
+    if lib().orc_mp_baseline(len(r), _ptr(r), float(mu), ctypes.addressof(b), _ptr(adv)) != 0:
+        raise ValueError("oracle maskpro_baseline: invalid arguments")
+    return adv, b.value
