@@ -9,7 +9,9 @@ There is no CPU fallback: without the built library every call raises.
 
 Entry points carry the C names (``maskgs_fwd`` ...).  Citations refer to the
 summary page "MaskLLM: Learnable Semi-Structured Sparsity for Large Language
-Models" (paper-graph-ui summary of arXiv 2409.17481).
+Models" (paper-graph-ui summary of arXiv 2409.17481); the ``maskpro_*`` entry
+points (``include/maskpro.h``) follow the summary page "MaskPro: Linear-Space
+Probabilistic Learning for Strict (N:M)-Sparsity on LLMs" (atlas.scime.ai).
 """
 from __future__ import annotations
 
@@ -37,7 +39,8 @@ MASKGS_HARD_SAMPLE = 2
 EXPORTS = ("maskgs_abi_version", "maskgs_status_str", "maskgs_candidates", "maskgs_fwd",
            "maskgs_fwd_hard",
            "maskgs_bwd", "maskgs_bwd_adamw", "maskgs_mask_stats", "maskgs_reg_reduce", "maskgs_hard_extract", "maskgs_prior_init",
-           "maskgs_debug_philox", "maskgs_debug_gumbel")
+           "maskgs_debug_philox", "maskgs_debug_gumbel",
+           "maskpro_fwd", "maskpro_bwd", "maskpro_init", "maskpro_baseline")
 
 
 class MaskgsError(RuntimeError):
@@ -63,6 +66,11 @@ class AdamWParams(ctypes.Structure):
     """maskgs_adamw_params: lr, beta1, beta2, eps, weight decay, update count t."""
     _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
                 ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("t", ctypes.c_uint32)]
+
+
+class DrawParams(ctypes.Structure):
+    """maskpro_draw_params: Philox seed and step, flags."""
+    _fields_ = [("seed", ctypes.c_uint64), ("step", ctypes.c_uint32), ("flags", ctypes.c_uint32)]
 
 
 _lib = None
@@ -98,6 +106,11 @@ def load_library(path: str = LIB_PATH):
     L.maskgs_debug_philox.argtypes = [c.c_uint64, c.c_uint32, c.c_uint32, c.c_uint64, c.c_int64,
                                       P, P]
     L.maskgs_debug_gumbel.argtypes = [P, c.c_int64, P, P]
+    L.maskpro_fwd.argtypes = [DP, c.POINTER(DrawParams), P, c.c_int, P, P, c.c_int, P, P, P]
+    L.maskpro_bwd.argtypes = [DP, c.POINTER(DrawParams), P, P, c.c_float, P, c.c_int32, P]
+    L.maskpro_init.argtypes = [DP, P, P, c.c_int, c.c_float, P, P]
+    L.maskpro_baseline.argtypes = [c.c_double, c.c_double, c.POINTER(c.c_double),
+                                   c.POINTER(c.c_double)]
     for name in EXPORTS:
         if name not in ("maskgs_status_str",):
             getattr(L, name).restype = c.c_int
@@ -360,3 +373,87 @@ def maskgs_debug_gumbel(words, g, stream=None):
         _ptr(words, "words", torch.int32), words.numel(),
         _ptr(g, "g", torch.float32, words.numel()), _stream(stream)))
     return g
+
+
+# --------------------------------------------------------------------------
+# Linear-space mask learner (include/maskpro.h; MaskPro summary page,
+# "Approach" and "Limitations")
+# --------------------------------------------------------------------------
+def draw_params(seed=0, step=0, flags=0) -> DrawParams:
+    return DrawParams(seed, step, flags)
+
+
+def _order_dtypes(m):
+    torch = _torch()
+    if m == 4:
+        return torch.uint8
+    return tuple(d for d in (torch.int16, getattr(torch, "uint16", None)) if d is not None)
+
+
+def maskpro_fwd(t: Tensor, p: DrawParams, pi, w=None, out=None, mask_bits=None, order=None,
+                stream=None):
+    """Ordered draw of N of M positions per block (Gumbel-top-k on pi + g) and
+    the hard-masked weights; pi fp32 [B, M]; order: uint8 [B] (2:4) or
+    int16/uint16 [B] (4:8)."""
+    torch = _torch()
+    dev = pi.device
+    B = t.nblocks
+    w_dt = _dtype_code(w) if w is not None else MASKGS_BF16
+    o_dt = _dtype_code(out) if out is not None else MASKGS_BF16
+    _check("maskpro_fwd", load_library().maskpro_fwd(
+        ctypes.byref(t.desc()), ctypes.byref(p), _ptr(w, "w", numel=t.rows * t.cols, device=dev),
+        w_dt, _ptr(pi, "pi", torch.float32, B * t.m, dev),
+        _ptr(out, "out", numel=t.rows * t.cols, device=dev), o_dt,
+        _ptr(mask_bits, "mask_bits", torch.uint8, (B * t.m + 7) // 8, dev),
+        _ptr(order, "order", _order_dtypes(t.m), B, dev), _stream(stream)))
+    return out
+
+
+def maskpro_bwd(t: Tensor, p: DrawParams, pi, advantage: float, dpi, order=None,
+                accumulate=False, stream=None):
+    """Policy gradient advantage * dlogp(draw)/dpi into dpi fp32 [B, M]; the draw
+    is `order` (maskpro_fwd's) or drawn again from pi and p."""
+    torch = _torch()
+    dev = pi.device
+    B = t.nblocks
+    _check("maskpro_bwd", load_library().maskpro_bwd(
+        ctypes.byref(t.desc()), ctypes.byref(p), _ptr(pi, "pi", torch.float32, B * t.m, dev),
+        _ptr(order, "order", _order_dtypes(t.m), B, dev), float(advantage),
+        _ptr(dpi, "dpi", torch.float32, B * t.m, dev), 1 if accumulate else 0, _stream(stream)))
+    return dpi
+
+
+def maskpro_init(t: Tensor, pi, c: float, prior_bits=None, w=None, stream=None):
+    """Initial logits: c at the initial mask's kept positions, 0 elsewhere."""
+    torch = _torch()
+    dev = pi.device
+    B = t.nblocks
+    w_dt = _dtype_code(w) if w is not None else MASKGS_BF16
+    _check("maskpro_init", load_library().maskpro_init(
+        ctypes.byref(t.desc()),
+        _ptr(prior_bits, "prior_bits", torch.uint8, (B * t.m + 7) // 8, dev),
+        _ptr(w, "w", numel=t.rows * t.cols, device=dev), w_dt, float(c),
+        _ptr(pi, "pi", torch.float32, B * t.m, dev), _stream(stream)))
+    return pi
+
+
+class Baseline:
+    """Moving-average baseline of the loss residual (host scalars, computed by
+    the library's maskpro_baseline)."""
+
+    def __init__(self, mu: float, value: float = 0.0):
+        self.mu = float(mu)
+        self.value = float(value)
+
+    def step(self, residual: float) -> float:
+        return maskpro_baseline(self, residual)
+
+
+def maskpro_baseline(state: Baseline, residual: float) -> float:
+    """Returns the advantage residual - baseline, then moves the baseline."""
+    b = ctypes.c_double(state.value)
+    adv = ctypes.c_double(0.0)
+    _check("maskpro_baseline", load_library().maskpro_baseline(
+        float(residual), state.mu, ctypes.byref(b), ctypes.byref(adv)))
+    state.value = b.value
+    return adv.value

@@ -8,7 +8,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 REPO = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmaskgs.so")
-SOURCES = ["maskgs_api.hip", "maskgs_k24.hip", "maskgs_k48.hip", "maskgs_debug.hip"]
+SOURCES = ["maskgs_api.hip", "maskgs_k24.hip", "maskgs_k48.hip", "maskgs_debug.hip",
+           "maskpro_k.hip"]
 
 # -ffp-contract=off: the noise contract fixes every rounding; fused multiply-adds
 # appear only where the source writes them.  Packed fp32 instructions are

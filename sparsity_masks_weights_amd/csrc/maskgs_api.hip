@@ -10,6 +10,8 @@
 #include "maskgs.h"
 #include "maskgs_device.hpp"
 #include "maskgs_launch.hpp"
+#include "maskpro.h"
+#include "maskpro_launch.hpp"
 
 namespace maskgs {
 
@@ -314,6 +316,94 @@ int maskgs_debug_gumbel(const uint32_t *words, int64_t n, float *g, hipStream_t 
     if (misaligned(words) || misaligned(g)) return MASKGS_E_ALIGN;
     if (n == 0) return MASKGS_OK;
     return launch_status(launch_debug_gumbel(words, n, g, stream));
+}
+
+/* ------------------------------------------------------------------------- */
+/* Linear-space mask learner (maskpro.h).                                    */
+/* ------------------------------------------------------------------------- */
+
+static int mp_common(const maskgs_tensor_desc *t, const maskpro_draw_params *p, MpArgs *a,
+                     int *m) {
+    Geometry g;
+    int rc = check_desc(t, &g);
+    if (rc) return rc;
+    if (!p) return MASKGS_E_NULL;
+    *a = MpArgs{};
+    a->nblocks = g.nblocks;
+    a->block_offset = g.block_offset;
+    a->tensor_id = g.tensor_id;
+    a->k0 = static_cast<uint32_t>(p->seed);
+    a->k1 = static_cast<uint32_t>(p->seed >> 32);
+    a->step = p->step;
+    a->no_noise = (p->flags & MASKGS_NO_NOISE) ? 1u : 0u;
+    *m = g.m;
+    return MASKGS_OK;
+}
+
+int maskpro_fwd(const maskgs_tensor_desc *t, const maskpro_draw_params *p, const void *w,
+                maskgs_dtype w_dt, const float *pi, void *out, maskgs_dtype out_dt,
+                uint8_t *mask_bits, void *order, hipStream_t stream) {
+    MpArgs a;
+    int m = 0;
+    int rc = mp_common(t, p, &a, &m);
+    if (rc) return rc;
+    if (a.nblocks == 0) return MASKGS_OK;
+    if (!pi || (out && !w)) return MASKGS_E_NULL;
+    if (out && (!valid_dtype(w_dt) || !valid_dtype(out_dt))) return MASKGS_E_DTYPE;
+    if (misaligned(pi) || misaligned(mask_bits) || misaligned(order) ||
+        (out && (misaligned(out) || misaligned(w))))
+        return MASKGS_E_ALIGN;
+    if (!out && !mask_bits && !order) return MASKGS_OK;
+    a.w = w;
+    a.pi = pi;
+    a.out = out;
+    a.bits = mask_bits;
+    a.order = order;
+    return launch_status(launch_mp_fwd(a, m, w_dt, out_dt, stream));
+}
+
+int maskpro_bwd(const maskgs_tensor_desc *t, const maskpro_draw_params *p, const float *pi,
+                const void *order, float advantage, float *dpi, int32_t accumulate,
+                hipStream_t stream) {
+    MpArgs a;
+    int m = 0;
+    int rc = mp_common(t, p, &a, &m);
+    if (rc) return rc;
+    if (!std::isfinite(advantage)) return MASKGS_E_RANGE;
+    if (a.nblocks == 0) return MASKGS_OK;
+    if (!pi || !dpi) return MASKGS_E_NULL;
+    if (misaligned(pi) || misaligned(order) || misaligned(dpi)) return MASKGS_E_ALIGN;
+    a.pi = pi;
+    a.order_in = order;
+    a.dpi = dpi;
+    a.adv = advantage;
+    a.accumulate = accumulate ? 1u : 0u;
+    return launch_status(launch_mp_bwd(a, m, stream));
+}
+
+int maskpro_init(const maskgs_tensor_desc *t, const uint8_t *prior_bits, const void *w,
+                 maskgs_dtype w_dt, float c, float *pi, hipStream_t stream) {
+    Geometry g;
+    int rc = check_desc(t, &g);
+    if (rc) return rc;
+    if (!std::isfinite(c)) return MASKGS_E_RANGE;
+    if (g.nblocks == 0) return MASKGS_OK;
+    if (!pi || (!prior_bits && !w)) return MASKGS_E_NULL;
+    if (!prior_bits && !valid_dtype(w_dt)) return MASKGS_E_DTYPE;
+    if (misaligned(pi) || misaligned(prior_bits) || (!prior_bits && misaligned(w)))
+        return MASKGS_E_ALIGN;
+    MpInitArgs a{prior_bits, w, c, pi, g.nblocks};
+    return launch_status(launch_mp_init(a, g.m, w_dt, stream));
+}
+
+int maskpro_baseline(double residual, double mu, double *baseline, double *advantage) {
+    if (!baseline || !advantage) return MASKGS_E_NULL;
+    if (!std::isfinite(residual) || !(mu >= 0.0 && mu <= 1.0) || !std::isfinite(*baseline))
+        return MASKGS_E_RANGE;
+    const double b = *baseline;
+    *advantage = residual - b;
+    *baseline = mu * b + (1.0 - mu) * residual;
+    return MASKGS_OK;
 }
 
 }  // extern "C"

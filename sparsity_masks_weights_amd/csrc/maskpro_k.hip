@@ -1,0 +1,388 @@
+// maskpro_k.hip -- gfx950 kernels of the linear-space N:M mask learner
+// (MaskPro summary page, "Approach"): M logits per block of M weights, an
+// ordered draw of N positions without replacement (Gumbel-top-k on the noise
+// contract of maskgs_device.hpp), the hard-masked weights, the policy
+// gradient of the draw's log-likelihood, and the initial logits.
+//
+// One lane per block.  A block's logits are 16 B (2:4) or 32 B (4:8) and its
+// weights 8 or 16 B (bf16), so consecutive lanes read consecutive 16-byte
+// vectors: every load and store is a coalesced dwordx2/dwordx4.  There is no
+// reuse between blocks, hence no LDS; the work per byte is the Philox stream
+// and two logarithms per position, which keeps the draw near the VALU/HBM
+// balance point.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "maskgs_device.hpp"
+#include "maskpro_launch.hpp"
+
+namespace maskgs {
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------------------
+// Vector access to one block of M elements of T.
+// ---------------------------------------------------------------------------
+template <typename T, int M>
+struct BlockIo;
+
+template <>
+struct BlockIo<float, 4> {
+    static __device__ __forceinline__ void load(const void *base, int64_t b, float (&v)[4]) {
+        const float4 x = reinterpret_cast<const float4 *>(base)[b];
+        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    }
+    static __device__ __forceinline__ void store(void *base, int64_t b, const float (&v)[4]) {
+        reinterpret_cast<float4 *>(base)[b] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    static __device__ __forceinline__ void load_raw(const void *base, int64_t b,
+                                                    uint32_t (&r)[4]) {
+        const uint4 x = reinterpret_cast<const uint4 *>(base)[b];
+        r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
+    }
+    static __device__ __forceinline__ void store_raw(void *base, int64_t b,
+                                                     const uint32_t (&r)[4]) {
+        reinterpret_cast<uint4 *>(base)[b] = make_uint4(r[0], r[1], r[2], r[3]);
+    }
+};
+
+template <>
+struct BlockIo<float, 8> {
+    static __device__ __forceinline__ void load(const void *base, int64_t b, float (&v)[8]) {
+        const float4 *p = reinterpret_cast<const float4 *>(base) + 2 * b;
+        const float4 x = p[0], y = p[1];
+        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+        v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+    }
+    static __device__ __forceinline__ void store(void *base, int64_t b, const float (&v)[8]) {
+        float4 *p = reinterpret_cast<float4 *>(base) + 2 * b;
+        p[0] = make_float4(v[0], v[1], v[2], v[3]);
+        p[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    static __device__ __forceinline__ void load_raw(const void *base, int64_t b,
+                                                    uint32_t (&r)[8]) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(base) + 2 * b;
+        const uint4 x = p[0], y = p[1];
+        r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
+        r[4] = y.x; r[5] = y.y; r[6] = y.z; r[7] = y.w;
+    }
+    static __device__ __forceinline__ void store_raw(void *base, int64_t b,
+                                                     const uint32_t (&r)[8]) {
+        uint4 *p = reinterpret_cast<uint4 *>(base) + 2 * b;
+        p[0] = make_uint4(r[0], r[1], r[2], r[3]);
+        p[1] = make_uint4(r[4], r[5], r[6], r[7]);
+    }
+};
+
+// bf16 blocks as raw 16-bit patterns, two per dword.
+template <>
+struct BlockIo<bf16_t, 4> {
+    static __device__ __forceinline__ void load_raw(const void *base, int64_t b,
+                                                    uint32_t (&r)[4]) {
+        const uint2 x = reinterpret_cast<const uint2 *>(base)[b];
+        r[0] = x.x & 0xFFFFu; r[1] = x.x >> 16; r[2] = x.y & 0xFFFFu; r[3] = x.y >> 16;
+    }
+    static __device__ __forceinline__ void store_raw(void *base, int64_t b,
+                                                     const uint32_t (&r)[4]) {
+        reinterpret_cast<uint2 *>(base)[b] = make_uint2(r[0] | (r[1] << 16), r[2] | (r[3] << 16));
+    }
+};
+
+template <>
+struct BlockIo<bf16_t, 8> {
+    static __device__ __forceinline__ void load_raw(const void *base, int64_t b,
+                                                    uint32_t (&r)[8]) {
+        const uint4 x = reinterpret_cast<const uint4 *>(base)[b];
+        const uint32_t d[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            r[2 * i] = d[i] & 0xFFFFu;
+            r[2 * i + 1] = d[i] >> 16;
+        }
+    }
+    static __device__ __forceinline__ void store_raw(void *base, int64_t b,
+                                                     const uint32_t (&r)[8]) {
+        reinterpret_cast<uint4 *>(base)[b] =
+            make_uint4(r[0] | (r[1] << 16), r[2] | (r[3] << 16), r[4] | (r[5] << 16),
+                       r[6] | (r[7] << 16));
+    }
+};
+
+// Raw element -> |w| ordering key (sign cleared) and -> output element.
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<float> {
+    static __device__ __forceinline__ uint32_t magnitude(uint32_t r) { return r & 0x7FFFFFFFu; }
+    // raw fp32 -> raw of the output type
+    static __device__ __forceinline__ uint32_t to_bf16(uint32_t r) {
+        return bf16_rne(__uint_as_float(r));
+    }
+    static __device__ __forceinline__ uint32_t to_f32(uint32_t r) { return r; }
+};
+
+template <>
+struct Elem<bf16_t> {
+    static __device__ __forceinline__ uint32_t magnitude(uint32_t r) { return r & 0x7FFFu; }
+    static __device__ __forceinline__ uint32_t to_bf16(uint32_t r) { return r; }
+    static __device__ __forceinline__ uint32_t to_f32(uint32_t r) { return r << 16; }
+};
+
+// ---------------------------------------------------------------------------
+// The draw: keys a_j = fp32(pi_j + g_j) (g_j from Philox word gb*M + j), then
+// N rounds of "first largest key among the positions not yet drawn" (strict
+// '>' from the lowest position, so ties and NaN keys go to the lower one).
+// pi_j - (-g_j) is bit-identical to pi_j + g_j.
+// ---------------------------------------------------------------------------
+template <int N, int M>
+__device__ __forceinline__ uint32_t draw(const float (&p)[M], uint64_t gb, const MpArgs &a,
+                                         int (&ord)[N]) {
+    float key[M];
+    if (a.no_noise) {
+#pragma unroll
+        for (int j = 0; j < M; ++j) key[j] = p[j];
+    } else {
+        uint32_t wd[M];
+        stream_words<M, 0>(gb * static_cast<uint64_t>(M / 4), a.step, a.tensor_id, a.k0, a.k1,
+                           wd);
+#pragma unroll
+        for (int j = 0; j < M; ++j) key[j] = p[j] - neg_gumbel(wd[j]);
+    }
+    uint32_t taken = 0;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        int best = -1;
+        float bv = 0.0f;
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            const bool take = !((taken >> j) & 1u) && (best < 0 || key[j] > bv);
+            best = take ? j : best;
+            bv = take ? key[j] : bv;
+        }
+        ord[k] = best;
+        taken |= 1u << best;
+    }
+    return taken;
+}
+
+template <int N, int M>
+__device__ __forceinline__ uint32_t pack_order(const int (&ord)[N]) {
+    constexpr int kBits = (M == 4) ? 2 : 3;
+    uint32_t v = 0;
+#pragma unroll
+    for (int k = 0; k < N; ++k) v |= static_cast<uint32_t>(ord[k]) << (kBits * k);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Forward: draw, masked weights, packed mask and draw order.
+// ---------------------------------------------------------------------------
+template <int N, int M, typename WT, typename OT>
+__global__ __launch_bounds__(kThreads) void mp_fwd_kernel(MpArgs a) {
+    const int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    const bool live = b < a.nblocks;
+    uint32_t keep = 0;
+    if (live) {
+        float p[M];
+        BlockIo<float, M>::load(a.pi, b, p);
+        int ord[N];
+        keep = draw<N, M>(p, a.block_offset + static_cast<uint64_t>(b), a, ord);
+        if (a.out) {
+            uint32_t r[M], o[M];
+            BlockIo<WT, M>::load_raw(a.w, b, r);
+#pragma unroll
+            for (int j = 0; j < M; ++j) {
+                const uint32_t v = (sizeof(OT) == 2) ? Elem<WT>::to_bf16(r[j])
+                                                     : Elem<WT>::to_f32(r[j]);
+                o[j] = ((keep >> j) & 1u) ? v : 0u;
+            }
+            BlockIo<OT, M>::store_raw(a.out, b, o);
+        }
+        if (a.order) {
+            if (M == 4)
+                static_cast<uint8_t *>(a.order)[b] = static_cast<uint8_t>(pack_order<N, M>(ord));
+            else
+                static_cast<uint16_t *>(a.order)[b] =
+                    static_cast<uint16_t>(pack_order<N, M>(ord));
+        }
+    }
+    if (a.bits) {
+        if (M == 8) {
+            if (live) a.bits[b] = static_cast<uint8_t>(keep);
+        } else {
+            // two 4-bit masks per byte: the even lane of each pair stores both
+            // (every lane of the wave reaches the shuffle; dead lanes give 0)
+            const uint32_t hi = __shfl_xor(keep, 1);
+            if (live && !(b & 1)) a.bits[b >> 1] = static_cast<uint8_t>(keep | (hi << 4));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Policy gradient of the ordered draw.  Round k (k = 1..N) runs over the
+// positions not yet drawn, with their own largest logit mx_k:
+//   e_l = exp(pi_l - mx_k),  Z = sum e_l  (>= 1),
+//   drawn position j_k:  += (Z - e_{j_k}) / Z  (summed over the others: no
+//                           cancellation), the "1 - exp(pi)/Z_k" term;
+//   every other one:     -= e_l / Z.
+// Then dpi = A * acc (+ dpi when accumulating).
+// ---------------------------------------------------------------------------
+template <int N, int M, bool ORDER_IN>
+__global__ __launch_bounds__(kThreads) void mp_bwd_kernel(MpArgs a) {
+    const int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (b >= a.nblocks) return;
+    float p[M];
+    BlockIo<float, M>::load(a.pi, b, p);
+    int ord[N];
+    if (ORDER_IN) {
+        constexpr int kBits = (M == 4) ? 2 : 3;
+        const uint32_t v = (M == 4) ? static_cast<const uint8_t *>(a.order_in)[b]
+                                    : static_cast<const uint16_t *>(a.order_in)[b];
+#pragma unroll
+        for (int k = 0; k < N; ++k) ord[k] = (v >> (kBits * k)) & ((1u << kBits) - 1u);
+    } else {
+        draw<N, M>(p, a.block_offset + static_cast<uint64_t>(b), a, ord);
+    }
+    float acc[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) acc[j] = 0.0f;
+    uint32_t taken = 0;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const int jk = ord[k];
+        float mx = -__builtin_huge_valf();
+#pragma unroll
+        for (int l = 0; l < M; ++l)
+            if (!((taken >> l) & 1u)) mx = __builtin_fmaxf(mx, p[l]);
+        float e[M];
+        float z = 0.0f, zo = 0.0f;
+#pragma unroll
+        for (int l = 0; l < M; ++l) {
+            const bool open = !((taken >> l) & 1u);
+            e[l] = open ? __expf(p[l] - mx) : 0.0f;
+            z += e[l];
+            zo += (l == jk) ? 0.0f : e[l];
+        }
+        const float inv = 1.0f / z;
+#pragma unroll
+        for (int l = 0; l < M; ++l) acc[l] -= (l == jk) ? 0.0f : e[l] * inv;
+#pragma unroll
+        for (int l = 0; l < M; ++l)
+            if (l == jk) acc[l] += zo * inv;
+        taken |= 1u << jk;
+    }
+    float d[M];
+    if (a.accumulate) {
+        BlockIo<float, M>::load(a.dpi, b, d);
+#pragma unroll
+        for (int j = 0; j < M; ++j) d[j] = d[j] + a.adv * acc[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < M; ++j) d[j] = a.adv * acc[j];
+    }
+    BlockIo<float, M>::store(a.dpi, b, d);
+}
+
+// ---------------------------------------------------------------------------
+// Initial logits: c at the kept positions of the initial mask, 0 elsewhere.
+// The mask is the packed prior (LSB-first, M bits per block) or the magnitude
+// top-N of w (N rounds of "first largest |w| not yet kept").
+// ---------------------------------------------------------------------------
+template <int N, int M, typename WT>
+__global__ __launch_bounds__(kThreads) void mp_init_kernel(MpInitArgs a) {
+    const int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (b >= a.nblocks) return;
+    uint32_t keep = 0;
+    if (a.prior_bits) {
+        if (M == 8)
+            keep = a.prior_bits[b];
+        else
+            keep = (a.prior_bits[b >> 1] >> (4 * (b & 1))) & 0xFu;
+    } else {
+        uint32_t r[M], mag[M];
+        BlockIo<WT, M>::load_raw(a.w, b, r);
+#pragma unroll
+        for (int j = 0; j < M; ++j) mag[j] = Elem<WT>::magnitude(r[j]);
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            int best = -1;
+            uint32_t bv = 0;
+#pragma unroll
+            for (int j = 0; j < M; ++j) {
+                const bool take = !((keep >> j) & 1u) && (best < 0 || mag[j] > bv);
+                best = take ? j : best;
+                bv = take ? mag[j] : bv;
+            }
+            keep |= 1u << best;
+        }
+    }
+    float v[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) v[j] = ((keep >> j) & 1u) ? a.c : 0.0f;
+    BlockIo<float, M>::store(a.pi, b, v);
+}
+
+unsigned blocks_for(int64_t nblocks) {
+    return static_cast<unsigned>((nblocks + kThreads - 1) / kThreads);
+}
+
+template <int N, int M, typename WT>
+hipError_t fwd_out(const MpArgs &a, maskgs_dtype out_dt, hipStream_t s) {
+    if (out_dt == MASKGS_BF16)
+        hipLaunchKernelGGL((mp_fwd_kernel<N, M, WT, bf16_t>), dim3(blocks_for(a.nblocks)),
+                           dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((mp_fwd_kernel<N, M, WT, float>), dim3(blocks_for(a.nblocks)),
+                           dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int N, int M>
+hipError_t fwd_nm(const MpArgs &a, maskgs_dtype w_dt, maskgs_dtype out_dt, hipStream_t s) {
+    if (w_dt == MASKGS_F32) return fwd_out<N, M, float>(a, out_dt, s);
+    return fwd_out<N, M, bf16_t>(a, out_dt, s);
+}
+
+template <int N, int M>
+hipError_t bwd_nm(const MpArgs &a, hipStream_t s) {
+    if (a.order_in)
+        hipLaunchKernelGGL((mp_bwd_kernel<N, M, true>), dim3(blocks_for(a.nblocks)),
+                           dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((mp_bwd_kernel<N, M, false>), dim3(blocks_for(a.nblocks)),
+                           dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int N, int M>
+hipError_t init_nm(const MpInitArgs &a, maskgs_dtype w_dt, hipStream_t s) {
+    if (a.prior_bits || w_dt == MASKGS_BF16)
+        hipLaunchKernelGGL((mp_init_kernel<N, M, bf16_t>), dim3(blocks_for(a.nblocks)),
+                           dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((mp_init_kernel<N, M, float>), dim3(blocks_for(a.nblocks)),
+                           dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mp_fwd(const MpArgs &a, int m, maskgs_dtype w_dt, maskgs_dtype out_dt,
+                         hipStream_t s) {
+    // without an output the weight type is irrelevant: use one instantiation
+    if (!a.out) w_dt = out_dt = MASKGS_BF16;
+    return m == 4 ? fwd_nm<2, 4>(a, w_dt, out_dt, s) : fwd_nm<4, 8>(a, w_dt, out_dt, s);
+}
+
+hipError_t launch_mp_bwd(const MpArgs &a, int m, hipStream_t s) {
+    return m == 4 ? bwd_nm<2, 4>(a, s) : bwd_nm<4, 8>(a, s);
+}
+
+hipError_t launch_mp_init(const MpInitArgs &a, int m, maskgs_dtype w_dt, hipStream_t s) {
+    return m == 4 ? init_nm<2, 4>(a, w_dt, s) : init_nm<4, 8>(a, w_dt, s);
+}
+
+}  // namespace maskgs

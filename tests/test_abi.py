@@ -1,17 +1,19 @@
 """Host-side checks of the C ABI (no GPU needed): the library loads, exports
-every entry point that include/maskgs.h declares, and rejects bad arguments
-with the documented status before anything is launched."""
+every entry point that include/*.h declares, and rejects bad arguments with
+the documented status before anything is launched."""
 import ctypes
+import glob
 import os
 import re
 
+import numpy as np
 import pytest
 
 from conftest import REPO
 
 import sparsity_masks_weights_amd as mg
 
-HEADER = os.path.join(REPO, "include", "maskgs.h")
+HEADERS = sorted(glob.glob(os.path.join(REPO, "include", "*.h")))
 
 
 @pytest.fixture(scope="module")
@@ -20,7 +22,9 @@ def L():
 
 
 def test_exports_every_declared_symbol(L):
-    decl = set(re.findall(r"\b(maskgs_\w+)\s*\(", open(HEADER).read()))
+    text = "".join(open(h).read() for h in HEADERS)
+    decl = set(re.findall(r"\b(mask(?:gs|pro)_\w+)\s*\(", text))
+    assert len(HEADERS) == 2
     assert decl == set(mg.EXPORTS)
     for name in decl:
         assert hasattr(L, name), name
@@ -154,6 +158,57 @@ def test_hard_sample_needs_recomputed_soft_index(L):
     opt = mg.AdamWParams(5e-4, 0.9, 0.999, 1e-8, 0.1, 1)
     assert L.maskgs_bwd_adamw(bd, bp, A, 1, A, A, A, 1, 1e-5, A, A, ctypes.byref(opt),
                               None) == mg.MASKGS_E_UNSUPPORTED
+
+
+def test_maskpro_validation(L):
+    d = mg.TensorDesc(2, 4, 8, 16, 0, 0)
+    p = mg.DrawParams(0, 0, 0)
+    bd, bp = ctypes.byref(d), ctypes.byref(p)
+    fwd = L.maskpro_fwd
+    assert fwd(bd, None, A, 1, A, A, 1, None, None, None) == mg.MASKGS_E_NULL
+    assert fwd(bd, bp, A, 1, None, A, 1, None, None, None) == mg.MASKGS_E_NULL     # pi
+    assert fwd(bd, bp, None, 1, A, A, 1, None, None, None) == mg.MASKGS_E_NULL     # out needs w
+    assert fwd(bd, bp, A, 5, A, A, 1, None, None, None) == mg.MASKGS_E_DTYPE
+    assert fwd(bd, bp, A, 1, A + 4, A, 1, None, None, None) == mg.MASKGS_E_ALIGN
+    assert fwd(bd, bp, A, 1, A, None, 1, A + 1, None, None) == mg.MASKGS_E_ALIGN
+    assert fwd(ctypes.byref(mg.TensorDesc(3, 8, 8, 16, 0, 0)), bp, A, 1, A, A, 1, None, None,
+               None) == mg.MASKGS_E_UNSUPPORTED
+    assert fwd(ctypes.byref(mg.TensorDesc(2, 4, 8, 18, 0, 0)), bp, A, 1, A, A, 1, None, None,
+               None) == mg.MASKGS_E_SHAPE
+    # nothing requested, or nothing to do: OK without a launch
+    assert fwd(bd, bp, None, 9, A, None, 9, None, None, None) == mg.MASKGS_OK
+    e = ctypes.byref(mg.TensorDesc(4, 8, 0, 16, 0, 0))
+    assert fwd(e, bp, None, 1, None, None, 1, None, None, None) == mg.MASKGS_OK
+    bwd = L.maskpro_bwd
+    assert bwd(bd, bp, None, None, 1.0, A, 0, None) == mg.MASKGS_E_NULL
+    assert bwd(bd, bp, A, None, 1.0, None, 0, None) == mg.MASKGS_E_NULL
+    assert bwd(bd, bp, A, None, float("nan"), A, 0, None) == mg.MASKGS_E_RANGE
+    assert bwd(bd, bp, A, None, float("inf"), A, 0, None) == mg.MASKGS_E_RANGE
+    assert bwd(bd, bp, A, A + 2, 1.0, A, 0, None) == mg.MASKGS_E_ALIGN
+    assert bwd(e, bp, None, None, 1.0, None, 0, None) == mg.MASKGS_OK
+    ini = L.maskpro_init
+    assert ini(bd, None, None, 1, 3.0, A, None) == mg.MASKGS_E_NULL
+    assert ini(bd, A, None, 1, 3.0, None, None) == mg.MASKGS_E_NULL
+    assert ini(bd, None, A, 7, 3.0, A, None) == mg.MASKGS_E_DTYPE
+    assert ini(bd, A, None, 1, float("inf"), A, None) == mg.MASKGS_E_RANGE
+    assert ini(bd, A, None, 1, 3.0, A + 8, None) == mg.MASKGS_E_ALIGN
+
+
+def test_maskpro_baseline_matches_oracle(orc):
+    """maskpro_baseline is host arithmetic: checked here against the oracle."""
+    rng = np.random.default_rng(4)
+    res = rng.standard_normal(50) * 3.0
+    ref, bref = orc.maskpro_baseline(res, mu=0.95)
+    st = mg.Baseline(mu=0.95)
+    got = np.array([st.step(r) for r in res])
+    assert np.array_equal(got, ref) and st.value == bref
+    b = ctypes.c_double(0.0)
+    a = ctypes.c_double(0.0)
+    L = mg.load_library()
+    assert L.maskpro_baseline(1.0, 1.5, ctypes.byref(b), ctypes.byref(a)) == mg.MASKGS_E_RANGE
+    assert L.maskpro_baseline(float("nan"), 0.5, ctypes.byref(b),
+                              ctypes.byref(a)) == mg.MASKGS_E_RANGE
+    assert L.maskpro_baseline(1.0, 0.5, None, ctypes.byref(a)) == mg.MASKGS_E_NULL
 
 
 def test_python_wrapper_refuses_cpu_tensors():

@@ -116,8 +116,8 @@ def _gen(device, seed):
 
 
 def seed_for(tensor_id: int, what: str) -> int:
-    """Generator seed of one input stream: 1000 + 16*tensor_id + {W,z,G,base}."""
-    return 1000 + 16 * tensor_id + {"w": 0, "z": 1, "g": 2, "base": 3}[what]
+    """Generator seed of one input stream: 1000 + 16*tensor_id + {W,z,G,base,pi}."""
+    return 1000 + 16 * tensor_id + {"w": 0, "z": 1, "g": 2, "base": 3, "pi": 4}[what]
 
 
 def draw(shape, std, dtype, device, seed):
@@ -138,3 +138,15 @@ def tensor_inputs(wl: Workload, spec: TensorSpec, device, rows=None):
     z = draw((B, wl.k), wl.z_std, "f32", device, seed_for(spec.tensor_id, "z"))
     g = draw((rows, spec.cols), wl.g_std, wl.g_dtype, device, seed_for(spec.tensor_id, "g"))
     return w, z, g
+
+
+# Linear-space logits (one per weight, the MaskPro variant): N(0, 1), a spread
+# at which the draws of a block vary from step to step.
+PI_STD = 1.0
+
+
+def linear_logits(wl: Workload, spec: TensorSpec, device, rows=None):
+    """fp32 [B, M] logits of one tensor for the linear-space variant."""
+    rows = spec.rows if rows is None else rows
+    B = rows * spec.cols // wl.m
+    return draw((B, wl.m), PI_STD, "f32", device, seed_for(spec.tensor_id, "pi"))
