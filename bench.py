@@ -14,7 +14,8 @@ training step with the logit update fused into the backward
 reported under `train_step` (--no-train-step skips it), and one pass of the
 training diagnostics (maskgs_mask_stats) over every tensor under `diagnostics`,
 and the step with the hard Gumbel-max sample (straight-through backward) under
-`hard_sample_step`.
+`hard_sample_step`, and the step of the linear-space variant (M logits per
+block, Gumbel-top-k draw, policy gradient) under `linear_space_step`.
 
 Prints ONE JSON line.  `value` = 2:4 weight blocks per second through the whole
 step; `roofline` describes the kernel with the largest share of the step;
@@ -394,6 +395,74 @@ def main():
                                              * 1e-3) / 1e9, 1))
                  for k, v in hs.items()})
 
+    # ---- linear-space variant (maskpro_*): M logits per block ------------
+    # A step draws N of M positions per block (masked weights, packed mask,
+    # draw order), then forms the policy gradient of every tensor from a
+    # scalar advantage (the loss and its baseline come from the model, which is
+    # outside the path; a fixed advantage stands in).  The gradient reuses the
+    # logit-gradient buffers (K >= M floats per block).
+    from workloads import linear_logits
+    torch.cuda.empty_cache()
+    odt = torch.uint8 if M == 4 else torch.int16
+    ob = 1 if M == 4 else 2
+    mp_bufs = []
+    for d in bufs:
+        mp_bufs.append(dict(pi=linear_logits(wl, d["spec"], dev),
+                            order=torch.empty(d["B"], dtype=odt, device=dev),
+                            dpi=d["dz"].view(-1)[: d["B"] * M]))
+    torch.cuda.synchronize()
+    dp = mg.DrawParams(0, 0, 0)
+    dpref = ctypes.byref(dp)
+    adv = ctypes.c_float(0.1)
+    mp_bytes = {
+        "saved_order": {"fwd": M * wb + 4 * M + 2 * M + M / 8 + ob, "bwd": 4 * M + ob + 4 * M},
+        "redrawn": {"fwd": M * wb + 4 * M + 2 * M + M / 8, "bwd": 8 * M},
+    }
+    linear = {}
+    for mode, bpb in mp_bytes.items():
+        keep_order = mode == "saved_order"
+        ph = {"fwd": [], "bwd": []}
+        l0, l1 = ev(), ev()
+        for s_ in range(-args.warmup, args.steps):
+            if s_ == 0:
+                torch.cuda.synchronize()
+                l0.record(stream)
+            dp.step = s_ % (1 << 32)
+            for kind in ("fwd", "bwd"):
+                p0, p1 = ev(), ev()
+                p0.record(stream)
+                for d, e in zip(bufs, mp_bufs):
+                    dref = ctypes.byref(d["desc"])
+                    op = ptr(e["order"]) if keep_order else None
+                    if kind == "fwd":
+                        rc = L.maskpro_fwd(dref, dpref, ptr(d["w"]), bf, ptr(e["pi"]),
+                                           ptr(d["out"]), bf, ptr(d["bits"]), op, sptr)
+                    else:
+                        rc = L.maskpro_bwd(dref, dpref, ptr(e["pi"]), op, adv, ptr(e["dpi"]), 0,
+                                           sptr)
+                    if rc != 0:
+                        raise RuntimeError(f"maskpro {kind}: status {rc}")
+                p1.record(stream)
+                if s_ >= 0:
+                    ph[kind].append((p0, p1))
+        l1.record(stream)
+        torch.cuda.synchronize()
+        ms_l = l0.elapsed_time(l1) / args.steps
+        ks = {}
+        for kind, v in ph.items():
+            tot = sum(a.elapsed_time(b) for a, b in v) / args.steps
+            ks[kind] = dict(ms_per_step=round(tot, 4), algorithmic_bytes_per_block=bpb[kind],
+                            achieved_gbs=round(bpb[kind] * total_blocks / (tot * 1e-3) / 1e9, 1))
+        linear[mode] = dict(ms_per_step=round(ms_l, 3),
+                            value=round(total_blocks / (ms_l * 1e-3), 1), kernels=ks)
+    linear_step = dict(
+        what="maskpro_fwd (Gumbel-top-k draw of N of M positions on M fp32 logits per block; "
+             "masked weights, packed mask, draw order) then maskpro_bwd (policy gradient "
+             "A*dlogp of the ordered draw, A = 0.1), every tensor; saved_order reads the "
+             "forward's draw order, redrawn draws again in the backward",
+        logits=f"fp32 N(0,1), {M} per block", **linear)
+    del mp_bufs
+
     if args.calibrate_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
@@ -438,6 +507,7 @@ def main():
     }
     result["diagnostics"] = diagnostics
     result["hard_sample_step"] = hard_sample_step
+    result["linear_space_step"] = linear_step
     if train:
         result["train_step"] = {
             "what": "fwd with the hard mask fused in, then maskgs_bwd_adamw (backward fused with "

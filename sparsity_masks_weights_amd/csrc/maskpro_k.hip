@@ -223,19 +223,22 @@ __global__ __launch_bounds__(kThreads) void mp_fwd_kernel(MpArgs a) {
 
 // ---------------------------------------------------------------------------
 // Policy gradient of the ordered draw.  Round k (k = 1..N) runs over the
-// positions not yet drawn, with their own largest logit mx_k:
-//   e_l = exp(pi_l - mx_k),  Z = sum e_l  (>= 1),
-//   drawn position j_k:  += (Z - e_{j_k}) / Z  (summed over the others: no
-//                           cancellation), the "1 - exp(pi)/Z_k" term;
-//   every other one:     -= e_l / Z.
-// Then dpi = A * acc (+ dpi when accumulating).
+// positions not yet drawn, whose logits q_l are the inputs while drawn ones
+// are set to -inf (exp then gives exactly 0, so no per-position select):
+//   mx = max_l q_l,  e_l = exp(q_l - mx),  Z = sum e_l (in [1, M]),
+//   acc_l -= e_l / Z  for every position,
+// then the drawn position's logit becomes -inf.  Forming each round against
+// its own largest open logit keeps the dominant terms accurate whatever the
+// spread of the block.  Finally every drawn position gets its +1 (the
+// derivative of pi_{j_k}); the cancellation in 1 - e/Z is an absolute error
+// of one ulp of 1.  dpi = A * acc (+ dpi when accumulating).
 // ---------------------------------------------------------------------------
 template <int N, int M, bool ORDER_IN>
 __global__ __launch_bounds__(kThreads) void mp_bwd_kernel(MpArgs a) {
     const int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
     if (b >= a.nblocks) return;
-    float p[M];
-    BlockIo<float, M>::load(a.pi, b, p);
+    float q[M];
+    BlockIo<float, M>::load(a.pi, b, q);
     int ord[N];
     if (ORDER_IN) {
         constexpr int kBits = (M == 4) ? 2 : 3;
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void mp_bwd_kernel(MpArgs a) {
 #pragma unroll
         for (int k = 0; k < N; ++k) ord[k] = (v >> (kBits * k)) & ((1u << kBits) - 1u);
     } else {
-        draw<N, M>(p, a.block_offset + static_cast<uint64_t>(b), a, ord);
+        draw<N, M>(q, a.block_offset + static_cast<uint64_t>(b), a, ord);
     }
     float acc[M];
 #pragma unroll
@@ -252,28 +255,28 @@ __global__ __launch_bounds__(kThreads) void mp_bwd_kernel(MpArgs a) {
     uint32_t taken = 0;
 #pragma unroll
     for (int k = 0; k < N; ++k) {
-        const int jk = ord[k];
-        float mx = -__builtin_huge_valf();
+        float mx = q[0];
 #pragma unroll
-        for (int l = 0; l < M; ++l)
-            if (!((taken >> l) & 1u)) mx = __builtin_fmaxf(mx, p[l]);
+        for (int l = 1; l < M; ++l) mx = __builtin_fmaxf(mx, q[l]);
         float e[M];
-        float z = 0.0f, zo = 0.0f;
+        float z = 0.0f;
 #pragma unroll
         for (int l = 0; l < M; ++l) {
-            const bool open = !((taken >> l) & 1u);
-            e[l] = open ? __expf(p[l] - mx) : 0.0f;
+            e[l] = __expf(q[l] - mx);
             z += e[l];
-            zo += (l == jk) ? 0.0f : e[l];
         }
-        const float inv = 1.0f / z;
+        const float inv = __builtin_amdgcn_rcpf(z);
 #pragma unroll
-        for (int l = 0; l < M; ++l) acc[l] -= (l == jk) ? 0.0f : e[l] * inv;
-#pragma unroll
-        for (int l = 0; l < M; ++l)
-            if (l == jk) acc[l] += zo * inv;
+        for (int l = 0; l < M; ++l) acc[l] = __builtin_fmaf(-e[l], inv, acc[l]);
+        const int jk = ord[k];
         taken |= 1u << jk;
+        if (k + 1 < N) {
+#pragma unroll
+            for (int l = 0; l < M; ++l) q[l] = (l == jk) ? -__builtin_huge_valf() : q[l];
+        }
     }
+#pragma unroll
+    for (int l = 0; l < M; ++l) acc[l] += ((taken >> l) & 1u) ? 1.0f : 0.0f;
     float d[M];
     if (a.accumulate) {
         BlockIo<float, M>::load(a.dpi, b, d);
