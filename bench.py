@@ -461,6 +461,8 @@ def main():
              "A*dlogp of the ordered draw, A = 0.1), every tensor; saved_order reads the "
              "forward's draw order, redrawn draws again in the backward",
         logits=f"fp32 N(0,1), {M} per block", **linear)
+    if not args.no_cpu_baseline:
+        linear_step["cpu_baseline"] = cpu_baseline_linear(wl, bufs, mp_bufs)
     del mp_bufs
 
     if args.calibrate_copy:
@@ -560,6 +562,42 @@ def cpu_baseline(wl, bufs, mg, min_secs=10.0):
             "kind": "oracle",
             "sample": f"first {layers} layer(s) of the same workload ({tensors} tensors, "
                       f"{blocks} blocks): fwd + bwd + hard extract, {secs:.1f} s of CPU time"}
+
+
+def cpu_baseline_linear(wl, bufs, mp_bufs, min_secs=8.0):
+    """The CPU oracle of the linear-space variant (one thread) on whole tensors
+    of the workload, in order, until at least `min_secs` of CPU work: draw +
+    masked weights, then the policy gradient of the saved draw order."""
+    import numpy as np
+    import torch
+    import oracle
+
+    blocks = 0
+    secs = 0.0
+    tensors = 0
+    for d, e in zip(bufs, mp_bufs):
+        if tensors and secs >= min_secs:
+            break
+        spec = d["spec"]
+        if d["w"].dtype == torch.bfloat16:
+            wf = oracle.widen_bf16(d["w"].view(torch.int16).cpu().numpy().view(np.uint16))
+        else:
+            wf = d["w"].cpu().numpy()
+        wf = wf.reshape(spec.rows, spec.cols)
+        pf = e["pi"].cpu().numpy()
+        kw = dict(seed=0, step=0, tensor_id=spec.tensor_id)
+        t = time.perf_counter()
+        f = oracle.maskpro_fwd(wl.n, wl.m, wf, pf, **kw)
+        oracle.maskpro_grad(wl.n, wl.m, pf, spec.rows, spec.cols, advantage=0.1,
+                            order=f["order"])
+        secs += time.perf_counter() - t
+        blocks += d["B"]
+        tensors += 1
+        del wf, pf, f
+    return {"value": round(blocks / secs, 1), "unit": "weight-blocks/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"first {tensors} tensor(s) of the same workload ({blocks} blocks): draw + "
+                      f"masked weights + policy gradient, {secs:.1f} s of CPU time"}
 
 
 if __name__ == "__main__":
