@@ -60,12 +60,25 @@ struct Cands<4, 8> {
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
 // Easy as 1, 2, 3", SC'11).  The key is uniform across a launch, so the
-// compiler keeps its schedule in scalar registers.
+// compiler keeps its schedule in scalar registers (the xor3 operand).
 // ---------------------------------------------------------------------------
 constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
 constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
 constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;
 constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
+
+// a ^ b ^ c, c uniform.  On gfx950 one v_bitop3_b32 (truth table 0x96 is the
+// three-input xor); the compiler forms it for some bit patterns but not for a
+// chained xor, which would cost two instructions per Philox output word.
+MASKGS_HD uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint32_t r;
+    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(c));
+    return r;
+#else
+    return a ^ b ^ c;
+#endif
+}
 
 MASKGS_HD void philox10(uint32_t &c0, uint32_t &c1, uint32_t &c2, uint32_t &c3, uint32_t k0,
                         uint32_t k1) {
@@ -74,8 +87,8 @@ MASKGS_HD void philox10(uint32_t &c0, uint32_t &c1, uint32_t &c2, uint32_t &c3, 
         // 32x32 -> 64-bit products: one v_mad_u64_u32 each on gfx950
         const uint64_t p0 = static_cast<uint64_t>(c0) * kPhiloxM0;
         const uint64_t p1 = static_cast<uint64_t>(c2) * kPhiloxM1;
-        const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n0 = xor3(static_cast<uint32_t>(p1 >> 32), c1, k0);
+        const uint32_t n2 = xor3(static_cast<uint32_t>(p0 >> 32), c3, k1);
         c1 = static_cast<uint32_t>(p1);
         c3 = static_cast<uint32_t>(p0);
         c0 = n0;

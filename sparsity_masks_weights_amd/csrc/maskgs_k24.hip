@@ -170,9 +170,6 @@ __device__ __forceinline__ void nt_store(float4 *p, float4 v) {
     __builtin_nontemporal_store(v4f{v.x, v.y, v.z, v.w}, reinterpret_cast<v4f *>(p));
 }
 
-// Stores 12 floats per lane for the workgroup tile of pairs [base, base+256):
-// lanes stage their values in LDS, then the tile (contiguous in memory) is
-// written with coalesced 16 B stores.  Called by every lane of the workgroup.
 // Writes a lane's 12 values to its slot of the LDS tile (pair order).
 __device__ __forceinline__ void stage12(const float (&v)[12], float4 *lds) {
     const int t = threadIdx.x;
@@ -181,6 +178,38 @@ __device__ __forceinline__ void stage12(const float (&v)[12], float4 *lds) {
     lds[3 * t + 2] = make_float4(v[8], v[9], v[10], v[11]);
 }
 
+// Stores 12 floats per lane for the pairs [base, base + kThreads) of the
+// workgroup with coalesced 16 B stores, through LDS.  The 64 pairs of one wave
+// are one contiguous 3 KB span of the output and its own slice of the LDS
+// tile, so each wave transposes and stores its span alone: a wave's LDS
+// operations complete in order, and no workgroup barrier holds the other waves
+// (measured 2-9% faster than a workgroup-wide transpose in the forward and
+// backward).  Called by every lane of the wave.
+__device__ __forceinline__ void store12_wave(float *g, int64_t base, int64_t nblocks,
+                                             const float (&v)[12], float4 *lds) {
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    stage12(v, lds);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int64_t wbase = base + 64 * wv;  // first pair of this wave
+    const int64_t end = 2 * (wbase + 64) < nblocks ? 2 * (wbase + 64) : nblocks;
+    const int nf = end > 2 * wbase ? static_cast<int>((end - 2 * wbase) * 6) : 0;
+    const int n4 = nf >> 2;
+    float4 *dst = reinterpret_cast<float4 *>(g + wbase * 12);
+    const float4 *src = lds + 3 * 64 * wv;
+    for (int i = lane; i < n4; i += 64) nt_store(dst + i, src[i]);
+    if ((nf & 3) && lane == 0)
+        reinterpret_cast<float2 *>(dst)[2 * n4] = reinterpret_cast<const float2 *>(src)[2 * n4];
+    // the next stage12 of this wave must not overtake these reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The same store with a workgroup-wide transpose (two barriers); prior seeding,
+// which rewrites the logits it has just read, measured faster with it.
 __device__ __forceinline__ void store12_tile(float *g, int64_t base, int64_t nblocks,
                                              const float (&v)[12], float4 *lds) {
     const int t = threadIdx.x;
@@ -407,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void fwd24_kernel(FwdArgs a) {
             reg += static_cast<double>(racc);
             Io<OT>::store8(a.out, p, two, out);
         }
-        if (a.y) store12_tile(a.y, base, a.g.nblocks, y, stage);
+        if (a.y) store12_wave(a.y, base, a.g.nblocks, y, stage);
     }
     if (a.reg) reduce_add(reg, a.reg);
 }
@@ -479,20 +508,26 @@ __global__ __launch_bounds__(kThreads) void bwd24_kernel(BwdArgs a) {
             }
         }
         if (ADAMW) {
-            // the gradient tile goes through LDS into the AdamW update of the
-            // same logits (coalesced float4 streams of z and both moments)
+            // the gradient goes through LDS into the AdamW update of the same
+            // logits (coalesced float4 streams of z and both moments); each
+            // wave updates its own contiguous span, as in store12_wave
             stage12(dz, stage);
-            __syncthreads();
-            const int64_t end = 2 * (base + kThreads) < a.g.nblocks ? 2 * (base + kThreads)
-                                                                   : a.g.nblocks;
-            const int nf = static_cast<int>((end - 2 * base) * 6);
-            adamw_span<kThreads, 3 * kThreads, 3>(a.zu + base * 12, a.m1 + base * 12,
-                                                  a.m2 + base * 12,
-                                                  reinterpret_cast<const float *>(stage), nf,
-                                                  a.adam);
-            __syncthreads();
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int lane = threadIdx.x & 63;
+            const int wv = threadIdx.x >> 6;
+            const int64_t wbase = base + 64 * wv;
+            const int64_t end = 2 * (wbase + 64) < a.g.nblocks ? 2 * (wbase + 64) : a.g.nblocks;
+            const int nf = end > 2 * wbase ? static_cast<int>((end - 2 * wbase) * 6) : 0;
+            adamw_span<64, 3 * 64, 3>(a.zu + wbase * 12, a.m1 + wbase * 12, a.m2 + wbase * 12,
+                                      reinterpret_cast<const float *>(stage + 3 * 64 * wv), nf,
+                                      a.adam, lane);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         } else {
-            store12_tile(a.dz, base, a.g.nblocks, dz, stage);
+            store12_wave(a.dz, base, a.g.nblocks, dz, stage);
         }
     }
 }

@@ -568,7 +568,7 @@ __global__ __launch_bounds__(kWave) void bwd48_kernel(BwdArgs a) {
         if (ADAMW) {
             // the gradient tile in LDS feeds the AdamW update of the same logits
             adamw_span<kWave, kWave * kK / 4, 6>(a.zu + b0 * kK, a.m1 + b0 * kK, a.m2 + b0 * kK,
-                                                 tl, nb * kK, a.adam);
+                                                 tl, nb * kK, a.adam, lane);
         } else {
             tile_copy_out(a.dz, b0, nb, tl);
         }

@@ -127,14 +127,13 @@ __device__ __forceinline__ void adam_step4(float4 &z, float4 &m, float4 &v, floa
 
 // AdamW update of nf consecutive logits z[0..nf) (16-byte aligned, at most CAP
 // float4) whose gradients are at g[0..nf) in LDS, with their moments m1, m2.
-// Float4 number k*THREADS + t is handled by thread t; the loads of BATCH such
-// rounds are issued before any of them is used.  An odd float pair at the end
-// is handled by thread 0.  Every thread of the workgroup calls this after the
-// barrier that publishes g.
+// Float4 number k*THREADS + t is handled by lane t of the THREADS lanes that
+// share the span; the loads of BATCH such rounds are issued before any of them
+// is used.  An odd float pair at the end is handled by lane 0.  Every lane of
+// the span calls this once g is visible to all of them.
 template <int THREADS, int CAP, int BATCH>
 __device__ __forceinline__ void adamw_span(float *z, float *m1, float *m2, const float *g, int nf,
-                                           const Adam &a) {
-    const int t = threadIdx.x;
+                                           const Adam &a, int t) {
     const int n4 = nf >> 2;
     constexpr int kRounds = (CAP + THREADS - 1) / THREADS;
     for (int r0 = 0; r0 < kRounds; r0 += BATCH) {
