@@ -37,6 +37,13 @@ __device__ __forceinline__ void unpack_bf16x2(uint32_t v, float &lo, float &hi) 
     hi = __uint_as_float(v & 0xFFFF0000u);
 }
 
+// Selects among four register values without indexing an array (which would
+// place the array in scratch memory).
+__device__ __forceinline__ uint32_t pick4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
+                                          uint32_t pos) {
+    return pos == 0 ? r0 : pos == 1 ? r1 : pos == 2 ? r2 : r3;
+}
+
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
@@ -61,9 +68,10 @@ struct Io<bf16_t> {
             v[4] = v[5] = v[6] = v[7] = 0.0f;
         }
     }
-    // raw bit patterns, widened to 32 bits
-    static __device__ __forceinline__ void load8_raw(const void *base, int64_t p, bool two,
-                                                     uint32_t (&r)[8]) {
+    // load8 that also keeps the words as loaded: d[0..3] hold the pair's bf16
+    // values two per word (d[4..7] unused)
+    static __device__ __forceinline__ void load8(const void *base, int64_t p, bool two,
+                                                 float (&v)[8], uint32_t (&d)[8]) {
         const uint16_t *ptr = static_cast<const uint16_t *>(base) + p * 8;
         uint4 u = make_uint4(0, 0, 0, 0);
         if (two) {
@@ -73,16 +81,40 @@ struct Io<bf16_t> {
             u.x = h.x;
             u.y = h.y;
         }
-        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+        unpack_bf16x2(u.x, v[0], v[1]);
+        unpack_bf16x2(u.y, v[2], v[3]);
+        unpack_bf16x2(u.z, v[4], v[5]);
+        unpack_bf16x2(u.w, v[6], v[7]);
+        d[0] = u.x; d[1] = u.y; d[2] = u.z; d[3] = u.w;
+        d[4] = d[5] = d[6] = d[7] = 0u;
+    }
+    // raw bit patterns, widened to 32 bits (one per position)
+    static __device__ __forceinline__ void load8_raw(const void *base, int64_t p, bool two,
+                                                     uint32_t (&r)[8]) {
+        uint32_t d[8];
+        load8_words(base, p, two, d);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            r[2 * i] = w4[i] & 0xFFFFu;
-            r[2 * i + 1] = w4[i] >> 16;
+            r[2 * i] = d[i] & 0xFFFFu;
+            r[2 * i + 1] = d[i] >> 16;
         }
     }
+    // the words as loaded (the form load8 keeps), for the hard-mask pass
+    static __device__ __forceinline__ void load8_words(const void *base, int64_t p, bool two,
+                                                       uint32_t (&d)[8]) {
+        const uint16_t *ptr = static_cast<const uint16_t *>(base) + p * 8;
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (two) {
+            u = *reinterpret_cast<const uint4 *>(ptr);
+        } else {
+            const uint2 h = *reinterpret_cast<const uint2 *>(ptr);
+            u.x = h.x;
+            u.y = h.y;
+        }
+        d[0] = u.x; d[1] = u.y; d[2] = u.z; d[3] = u.w;
+        d[4] = d[5] = d[6] = d[7] = 0u;
+    }
     static __device__ __forceinline__ uint32_t magnitude(uint32_t raw) { return raw & 0x7FFFu; }
-    // bit pattern of a value that was widened from bf16 (exact)
-    static __device__ __forceinline__ uint32_t raw_of(float v) { return __float_as_uint(v) >> 16; }
     static __device__ __forceinline__ void store8(void *base, int64_t p, bool two,
                                                   const float (&v)[8]) {
         uint16_t *ptr = static_cast<uint16_t *>(base) + p * 8;
@@ -96,15 +128,22 @@ struct Io<bf16_t> {
         else
             *reinterpret_cast<uint2 *>(ptr) = make_uint2(u[0], u[1]);
     }
-    // 2 kept values per block: 4 raw values for the pair (2 if only one block)
+    // The 2 kept values of each block (positions lo < hi, given as the nibble
+    // lo | hi << 2) in ascending position, from the words as loaded: one
+    // byte permute per block picks bytes 2lo, 2lo+1, 2hi, 2hi+1 of its two
+    // words, so the output word is w_lo | w_hi << 16.
     static __device__ __forceinline__ void store_values(void *base, int64_t p, bool two,
-                                                        const uint32_t (&r)[4]) {
+                                                        const uint32_t (&d)[8], uint32_t lohi0,
+                                                        uint32_t lohi1) {
         uint16_t *ptr = static_cast<uint16_t *>(base) + p * 4;
-        const uint32_t a = r[0] | (r[1] << 16), b = r[2] | (r[3] << 16);
-        if (two)
-            *reinterpret_cast<uint2 *>(ptr) = make_uint2(a, b);
-        else
+        const uint32_t s0 = 0x01000100u + (lohi0 & 3u) * 0x0202u + (lohi0 >> 2) * 0x02020000u;
+        const uint32_t a = __builtin_amdgcn_perm(d[1], d[0], s0);
+        if (two) {
+            const uint32_t s1 = 0x01000100u + (lohi1 & 3u) * 0x0202u + (lohi1 >> 2) * 0x02020000u;
+            *reinterpret_cast<uint2 *>(ptr) = make_uint2(a, __builtin_amdgcn_perm(d[3], d[2], s1));
+        } else {
             *reinterpret_cast<uint32_t *>(ptr) = a;
+        }
     }
 };
 
@@ -129,23 +168,38 @@ struct Io<float> {
 #pragma unroll
         for (int i = 0; i < 8; ++i) r[i] = __float_as_uint(v[i]);
     }
+    static __device__ __forceinline__ void load8_words(const void *base, int64_t p, bool two,
+                                                       uint32_t (&d)[8]) {
+        load8_raw(base, p, two, d);
+    }
+    static __device__ __forceinline__ void load8(const void *base, int64_t p, bool two,
+                                                 float (&v)[8], uint32_t (&d)[8]) {
+        load8(base, p, two, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d[i] = __float_as_uint(v[i]);
+    }
     static __device__ __forceinline__ uint32_t magnitude(uint32_t raw) {
         return raw & 0x7FFFFFFFu;
     }
-    static __device__ __forceinline__ uint32_t raw_of(float v) { return __float_as_uint(v); }
     static __device__ __forceinline__ void store8(void *base, int64_t p, bool two,
                                                   const float (&v)[8]) {
         float *ptr = static_cast<float *>(base) + p * 8;
         *reinterpret_cast<float4 *>(ptr) = make_float4(v[0], v[1], v[2], v[3]);
         if (two) *reinterpret_cast<float4 *>(ptr + 4) = make_float4(v[4], v[5], v[6], v[7]);
     }
+    // The 2 kept values of each block (nibble lo | hi << 2), ascending.
     static __device__ __forceinline__ void store_values(void *base, int64_t p, bool two,
-                                                        const uint32_t (&r)[4]) {
+                                                        const uint32_t (&d)[8], uint32_t lohi0,
+                                                        uint32_t lohi1) {
         uint32_t *ptr = static_cast<uint32_t *>(base) + p * 4;
+        const uint32_t a = pick4(d[0], d[1], d[2], d[3], lohi0 & 3u);
+        const uint32_t b = pick4(d[0], d[1], d[2], d[3], lohi0 >> 2);
         if (two)
-            *reinterpret_cast<uint4 *>(ptr) = make_uint4(r[0], r[1], r[2], r[3]);
+            *reinterpret_cast<uint4 *>(ptr) =
+                make_uint4(a, b, pick4(d[4], d[5], d[6], d[7], lohi1 & 3u),
+                           pick4(d[4], d[5], d[6], d[7], lohi1 >> 2));
         else
-            *reinterpret_cast<uint2 *>(ptr) = make_uint2(r[0], r[1]);
+            *reinterpret_cast<uint2 *>(ptr) = make_uint2(a, b);
     }
 };
 
@@ -295,19 +349,34 @@ constexpr uint32_t kMaskNibbles24 = pack_nibbles24();
 
 __device__ __forceinline__ uint32_t cand_mask6(int k) { return (kMaskNibbles24 >> (4 * k)) & 0xFu; }
 
-// Selects among four register values without indexing an array (which would
-// place the array in scratch memory).
-__device__ __forceinline__ uint32_t pick4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
-                                          uint32_t pos) {
-    return pos == 0 ? r0 : pos == 1 ? r1 : pos == 2 ? r2 : r3;
+// The kept positions lo < hi of each candidate as the nibble lo | hi << 2 (the
+// 2-bit index format), packed like kMaskNibbles24.
+constexpr uint32_t pack_lohi24() {
+    uint32_t v = 0;
+    for (int i = 0; i < 6; ++i) {
+        int lo = -1, hi = -1;
+        for (int j = 0; j < 4; ++j)
+            if ((C24::mask[i] >> j) & 1u) {
+                if (lo < 0)
+                    lo = j;
+                else
+                    hi = j;
+            }
+        v |= static_cast<uint32_t>(lo | (hi << 2)) << (4 * i);
+    }
+    return v;
 }
+constexpr uint32_t kLoHi24 = pack_lohi24();
+static_assert(kLoHi24 == 0xE9DC84u, "kept positions of the page-order 2:4 candidates");
 
-// Hard mask of one pair from its logits z and raw weight bits r (r read only
-// when values are requested).
+__device__ __forceinline__ uint32_t cand_lohi6(int k) { return (kLoHi24 >> (4 * k)) & 0xFu; }
+
+// Hard mask of one pair from its logits z and the pair's weight words d (as
+// Io<WT>::load8_words gives them; read only when values are requested).
 template <typename WT>
 __device__ __forceinline__ void hard_pair(uint8_t *idx, uint8_t *bits, void *values,
                                           uint8_t *val_idx, int64_t p, bool two,
-                                          const float (&z)[12], const uint32_t (&r)[8]) {
+                                          const float (&z)[12], const uint32_t (&d)[8]) {
     const int k0 = first_argmax6(z), k1 = first_argmax6(z + 6);
     const uint32_t m0 = cand_mask6(k0), m1 = two ? cand_mask6(k1) : 0u;
     if (idx) {
@@ -317,16 +386,9 @@ __device__ __forceinline__ void hard_pair(uint8_t *idx, uint8_t *bits, void *val
             idx[2 * p] = static_cast<uint8_t>(k0);
     }
     if (bits) bits[p] = static_cast<uint8_t>(m0 | (m1 << 4));
-    const uint32_t lo0 = __builtin_ctz(m0), hi0 = 31 - __builtin_clz(m0);
-    const uint32_t lo1 = two ? __builtin_ctz(m1) : 0u, hi1 = two ? 31 - __builtin_clz(m1) : 0u;
-    if (val_idx)
-        val_idx[p] = static_cast<uint8_t>((lo0 | (hi0 << 2)) |
-                                          (two ? ((lo1 | (hi1 << 2)) << 4) : 0u));
-    if (values) {
-        const uint32_t v[4] = {pick4(r[0], r[1], r[2], r[3], lo0), pick4(r[0], r[1], r[2], r[3], hi0),
-                               pick4(r[4], r[5], r[6], r[7], lo1), pick4(r[4], r[5], r[6], r[7], hi1)};
-        Io<WT>::store_values(values, p, two, v);
-    }
+    const uint32_t lh0 = cand_lohi6(k0), lh1 = two ? cand_lohi6(k1) : 0u;
+    if (val_idx) val_idx[p] = static_cast<uint8_t>(lh0 | (lh1 << 4));
+    if (values) Io<WT>::store_values(values, p, two, d, lh0, lh1);
 }
 
 // Soft index of a pair (section 3.4, Eq. 6 and Algorithm 1 steps 1-2):
@@ -410,14 +472,12 @@ __global__ __launch_bounds__(kThreads) void fwd24_kernel(FwdArgs a) {
         if (p < npairs) {
             const bool two = 2 * p + 1 < a.g.nblocks;
             float w[8], z[12], out[8];
-            Io<WT>::load8(a.w, p, two, w);
+            uint32_t wd[8];
+            Io<WT>::load8(a.w, p, two, w, wd);
             load12(a.z, p, two, z);
             if (hard) {
                 // hard mask of the same logits (argmax of z, not of the sample)
-                uint32_t r[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) r[j] = Io<WT>::raw_of(w[j]);
-                hard_pair<WT>(a.idx, a.bits, a.values, a.val_idx, p, two, z, r);
+                hard_pair<WT>(a.idx, a.bits, a.values, a.val_idx, p, two, z, wd);
             }
             uint32_t hm[2];
             pair_sample<PHASE>(a.g, a.nz, p, z, y, hm);
@@ -584,7 +644,7 @@ __global__ __launch_bounds__(kThreads) void hard24_kernel(HardArgs a) {
         float z[12];
         uint32_t r[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
         load12(a.z, p, two, z);
-        if (a.values) Io<WT>::load8_raw(a.w, p, two, r);
+        if (a.values) Io<WT>::load8_words(a.w, p, two, r);
         hard_pair<WT>(a.idx, a.bits, a.values, a.val_idx, p, two, z, r);
     }
 }
