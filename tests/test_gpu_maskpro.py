@@ -77,6 +77,10 @@ CASES = [
     (4, 8, 37, 72, "bf16", "bf16", 3, 4, 11, 2, 1.0),     # 333 blocks: ragged
     (4, 8, 16, 128, "f32", "f32", 0, 0, 0, 0, -3.0),
     (4, 8, 130, 512, "bf16", "f32", 2, 3, 5, 1, 0.5),
+    # global block offsets past 2^40 and the largest step: the Philox counter's
+    # high word and the step word both in play
+    (2, 4, 33, 64, "bf16", "bf16", 2 ** 40 + 3, 7, 12345, 2 ** 32 - 1, 0.75),
+    (4, 8, 9, 64, "bf16", "bf16", 2 ** 45 + 1, 2, 99, 123456, 1.5),
 ]
 
 
