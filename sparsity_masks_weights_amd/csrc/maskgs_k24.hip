@@ -115,6 +115,14 @@ struct Io<bf16_t> {
         d[4] = d[5] = d[6] = d[7] = 0u;
     }
     static __device__ __forceinline__ uint32_t magnitude(uint32_t raw) { return raw & 0x7FFFu; }
+    // |w| ordering keys (sign cleared) of the 8 positions, from the loaded words
+    static __device__ __forceinline__ void mags8(const uint32_t (&d)[8], uint32_t (&mag)[8]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            mag[2 * i] = d[i] & 0x7FFFu;
+            mag[2 * i + 1] = (d[i] >> 16) & 0x7FFFu;
+        }
+    }
     static __device__ __forceinline__ void store8(void *base, int64_t p, bool two,
                                                   const float (&v)[8]) {
         uint16_t *ptr = static_cast<uint16_t *>(base) + p * 8;
@@ -180,6 +188,10 @@ struct Io<float> {
     }
     static __device__ __forceinline__ uint32_t magnitude(uint32_t raw) {
         return raw & 0x7FFFFFFFu;
+    }
+    static __device__ __forceinline__ void mags8(const uint32_t (&d)[8], uint32_t (&mag)[8]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mag[i] = d[i] & 0x7FFFFFFFu;
     }
     static __device__ __forceinline__ void store8(void *base, int64_t p, bool two,
                                                   const float (&v)[8]) {
@@ -796,8 +808,15 @@ __global__ __launch_bounds__(kThreads) void stats24_kernel(StatsArgs a) {
     for (int64_t p = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; p < npairs;
          p += stride) {
         const bool two = 2 * p + 1 < a.g.nblocks;
-        float z[12];
+        // every stream of the pair is requested before any is used, so one
+        // memory latency covers them (the pointer tests are uniform)
+        float z[12], d[12], w[8];
+        uint32_t wd[8];
+        uint32_t rb = 0;
         load12(a.z, p, two, z);
+        if (a.w) Io<WT>::load8(a.w, p, two, w, wd);
+        if (a.dz) load12(a.dz, p, two, d);
+        if (a.ref_bits) rb = a.ref_bits[p];
         int k0, k1;
         if (SAMPLED) {
             float a12[12];
@@ -809,19 +828,13 @@ __global__ __launch_bounds__(kThreads) void stats24_kernel(StatsArgs a) {
             k1 = first_argmax6(z + 6);
         }
         const uint32_t m0 = cand_mask6(k0), m1 = cand_mask6(k1);
-        if (a.ref_bits) {
-            const uint32_t rb = a.ref_bits[p];
+        if (a.ref_bits)
             acc[0] += static_cast<double>(((rb & 0xFu) != m0) + (two && ((rb >> 4) != m1)));
-        }
         acc[1] += static_cast<double>(max_prob6(z, a.kappa_log2e));
         if (two) acc[1] += static_cast<double>(max_prob6(z + 6, a.kappa_log2e));
         if (a.w) {
-            float w[8];
-            uint32_t r[8], mag[8];
-            Io<WT>::load8(a.w, p, two, w);
-            Io<WT>::load8_raw(a.w, p, two, r);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) mag[j] = Io<WT>::magnitude(r[j]);
+            uint32_t mag[8];
+            Io<WT>::mags8(wd, mag);
             acc[2] += kept_abs4(w, m0);
             acc[3] += kept_abs4(w, top2_of4(mag));
             if (two) {
@@ -830,8 +843,6 @@ __global__ __launch_bounds__(kThreads) void stats24_kernel(StatsArgs a) {
             }
         }
         if (a.dz) {
-            float d[12];
-            load12(a.dz, p, two, d);
             double s = 0.0;
 #pragma unroll
             for (int i = 0; i < 12; ++i) s += static_cast<double>(d[i]) * static_cast<double>(d[i]);
@@ -845,11 +856,18 @@ __global__ __launch_bounds__(kThreads) void stats24_kernel(StatsArgs a) {
 }
 
 template <typename K, typename A>
-hipError_t go(K kernel, const A &args, int64_t items, hipStream_t s) {
-    const unsigned grid = grid_for(items, kThreads, kWavesPerCU);
+hipError_t go(K kernel, const A &args, int64_t items, hipStream_t s,
+              int wg_per_cu = kWavesPerCU) {
+    const unsigned grid = grid_for(items, kThreads, wg_per_cu);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, s, args);
     return hipGetLastError();
 }
+
+// The diagnostics pass ends every workgroup with five fp64 atomics into one
+// 48-byte struct, which serialise at its L2 line: 2 workgroups per CU
+// (measured 125 us on 11008x4096) against 175 us at the grid cap of the
+// streaming kernels and 279 us at 16.
+constexpr int kStatsWgPerCU = 2;
 
 int phase_of(uint64_t block_offset) { return (block_offset & 1u) ? 2 : 0; }
 
@@ -927,11 +945,12 @@ hipError_t launch_prior24(const PriorArgs &a, maskgs_dtype w_dt, hipStream_t s) 
 template <int PHASE>
 hipError_t stats24_dispatch(const StatsArgs &a, bool sampled, maskgs_dtype w_dt, hipStream_t s) {
     const int64_t np = (a.g.nblocks + 1) >> 1;
+    const int c = kStatsWgPerCU;
     if (sampled)
-        return w_dt == MASKGS_F32 ? go(stats24_kernel<PHASE, float, true>, a, np, s)
-                                  : go(stats24_kernel<PHASE, bf16_t, true>, a, np, s);
-    return w_dt == MASKGS_F32 ? go(stats24_kernel<PHASE, float, false>, a, np, s)
-                              : go(stats24_kernel<PHASE, bf16_t, false>, a, np, s);
+        return w_dt == MASKGS_F32 ? go(stats24_kernel<PHASE, float, true>, a, np, s, c)
+                                  : go(stats24_kernel<PHASE, bf16_t, true>, a, np, s, c);
+    return w_dt == MASKGS_F32 ? go(stats24_kernel<PHASE, float, false>, a, np, s, c)
+                              : go(stats24_kernel<PHASE, bf16_t, false>, a, np, s, c);
 }
 
 hipError_t launch_stats24(const StatsArgs &a, bool sampled, maskgs_dtype w_dt, hipStream_t s) {

@@ -722,6 +722,18 @@ __global__ __launch_bounds__(kWave) void stats48_kernel(StatsArgs a) {
         const int nb = static_cast<int>(a.g.nblocks - b0 < kWave ? a.g.nblocks - b0 : kWave);
         const int64_t b = b0 + lane;
         tile_copy_in(a.z, b0, nb, reinterpret_cast<float *>(tile4));
+        // the block's weights and reference mask are requested with the tile,
+        // so the tile's wait covers them
+        float w[8];
+        uint32_t mag[8];
+        uint32_t rb = 0;
+        if (lane < nb) {
+            if (a.w) {
+                Io8<WT>::load(a.w, b, w);
+                Io8<WT>::load_mag(a.w, b, mag);
+            }
+            if (a.ref_bits) rb = a.ref_bits[b];
+        }
         lds_fill_wait();
         __syncthreads();
         if (lane < nb) {
@@ -737,7 +749,7 @@ __global__ __launch_bounds__(kWave) void stats48_kernel(StatsArgs a) {
                 key = argmax_key70(row);
             }
             const uint32_t mask = key & 0xFFu;
-            if (a.ref_bits) acc[0] += static_cast<double>(a.ref_bits[b] != mask);
+            if (a.ref_bits) acc[0] += static_cast<double>(rb != mask);
             float zmax = row[0];
 #pragma unroll
             for (int i = 1; i < kK; ++i) zmax = fmaxf(zmax, row[i]);
@@ -746,10 +758,6 @@ __global__ __launch_bounds__(kWave) void stats48_kernel(StatsArgs a) {
             for (int i = 0; i < kK; ++i) s += __builtin_amdgcn_exp2f((row[i] - zmax) * a.kappa_log2e);
             acc[1] += static_cast<double>(1.0f / s);
             if (a.w) {
-                float w[8];
-                uint32_t mag[8];
-                Io8<WT>::load(a.w, b, w);
-                Io8<WT>::load_mag(a.w, b, mag);
                 const uint32_t top = top4_of8(mag);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
@@ -760,13 +768,24 @@ __global__ __launch_bounds__(kWave) void stats48_kernel(StatsArgs a) {
             }
         }
         if (a.dz) {
-            // the tile's gradients, coalesced
+            // the tile's gradients, coalesced, six float4 per lane in flight
             const float *src = a.dz + b0 * kK;
             const int nf = nb * kK, n4 = nf >> 2;
-            for (int i = lane; i < n4; i += kWave) {
-                const float4 d = reinterpret_cast<const float4 *>(src)[i];
-                acc[4] += static_cast<double>(d.x) * d.x + static_cast<double>(d.y) * d.y +
-                          static_cast<double>(d.z) * d.z + static_cast<double>(d.w) * d.w;
+            constexpr int kBatch = 6;
+            for (int i0 = lane; i0 < n4; i0 += kBatch * kWave) {
+                float4 d[kBatch];
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k) {
+                    const int i = i0 + k * kWave;
+                    d[k] = i < n4 ? reinterpret_cast<const float4 *>(src)[i]
+                                  : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                }
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k)
+                    acc[4] += static_cast<double>(d[k].x) * d[k].x +
+                              static_cast<double>(d[k].y) * d[k].y +
+                              static_cast<double>(d[k].z) * d[k].z +
+                              static_cast<double>(d[k].w) * d[k].w;
             }
             if ((nf & 3) && lane == 0) {
                 const float2 d = reinterpret_cast<const float2 *>(src)[2 * n4];
@@ -797,8 +816,9 @@ __global__ __launch_bounds__(kWave) void stats48_kernel(StatsArgs a) {
 }
 
 template <typename Kern, typename A>
-hipError_t go(Kern kernel, const A &args, int64_t nblocks, hipStream_t s) {
-    const unsigned grid = grid_for((nblocks + kWave - 1) / kWave, 1, kWgPerCU);
+hipError_t go(Kern kernel, const A &args, int64_t nblocks, hipStream_t s,
+              int wg_per_cu = kWgPerCU) {
+    const unsigned grid = grid_for((nblocks + kWave - 1) / kWave, 1, wg_per_cu);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kWave), 0, s, args);
     return hipGetLastError();
 }
@@ -873,13 +893,20 @@ hipError_t launch_prior48(const PriorArgs &a, maskgs_dtype w_dt, hipStream_t s) 
     return go(prior48_kernel<bf16_t, false>, a, n, s);
 }
 
+// The diagnostics end every workgroup with fp64 atomics into one struct (one
+// L2 line): 8 single-wave workgroups per CU, the most that are resident at
+// once with a logit tile each, measured 2.5% faster than 16 and far faster
+// than 4 (1.6x slower).
+constexpr int kStatsWgPerCU = 8;
+
 hipError_t launch_stats48(const StatsArgs &a, bool sampled, maskgs_dtype w_dt, hipStream_t s) {
     const int64_t n = a.g.nblocks;
+    const int c = kStatsWgPerCU;
     if (sampled)
-        return w_dt == MASKGS_F32 ? go(stats48_kernel<float, true>, a, n, s)
-                                  : go(stats48_kernel<bf16_t, true>, a, n, s);
-    return w_dt == MASKGS_F32 ? go(stats48_kernel<float, false>, a, n, s)
-                              : go(stats48_kernel<bf16_t, false>, a, n, s);
+        return w_dt == MASKGS_F32 ? go(stats48_kernel<float, true>, a, n, s, c)
+                                  : go(stats48_kernel<bf16_t, true>, a, n, s, c);
+    return w_dt == MASKGS_F32 ? go(stats48_kernel<float, false>, a, n, s, c)
+                              : go(stats48_kernel<bf16_t, false>, a, n, s, c);
 }
 
 }  // namespace maskgs
