@@ -182,41 +182,47 @@ __device__ __forceinline__ uint32_t pack_order(const int (&ord)[N]) {
 // ---------------------------------------------------------------------------
 template <int N, int M, typename WT, typename OT>
 __global__ __launch_bounds__(kThreads) void mp_fwd_kernel(MpArgs a) {
-    const int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    const bool live = b < a.nblocks;
-    uint32_t keep = 0;
-    if (live) {
-        float p[M];
-        BlockIo<float, M>::load(a.pi, b, p);
-        int ord[N];
-        keep = draw<N, M>(p, a.block_offset + static_cast<uint64_t>(b), a, ord);
-        if (a.out) {
-            uint32_t r[M], o[M];
-            BlockIo<WT, M>::load_raw(a.w, b, r);
+    // grid-stride over workgroup-sized spans of blocks (the span base is
+    // uniform, so every lane of a wave reaches the cross-lane swap below)
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads; base < a.nblocks;
+         base += stride) {
+        const int64_t b = base + threadIdx.x;
+        const bool live = b < a.nblocks;
+        uint32_t keep = 0;
+        if (live) {
+            float p[M];
+            BlockIo<float, M>::load(a.pi, b, p);
+            int ord[N];
+            keep = draw<N, M>(p, a.block_offset + static_cast<uint64_t>(b), a, ord);
+            if (a.out) {
+                uint32_t r[M], o[M];
+                BlockIo<WT, M>::load_raw(a.w, b, r);
 #pragma unroll
-            for (int j = 0; j < M; ++j) {
-                const uint32_t v = (sizeof(OT) == 2) ? Elem<WT>::to_bf16(r[j])
-                                                     : Elem<WT>::to_f32(r[j]);
-                o[j] = ((keep >> j) & 1u) ? v : 0u;
+                for (int j = 0; j < M; ++j) {
+                    const uint32_t v = (sizeof(OT) == 2) ? Elem<WT>::to_bf16(r[j])
+                                                         : Elem<WT>::to_f32(r[j]);
+                    o[j] = ((keep >> j) & 1u) ? v : 0u;
+                }
+                BlockIo<OT, M>::store_raw(a.out, b, o);
             }
-            BlockIo<OT, M>::store_raw(a.out, b, o);
+            if (a.order) {
+                if (M == 4)
+                    static_cast<uint8_t *>(a.order)[b] = static_cast<uint8_t>(pack_order<N, M>(ord));
+                else
+                    static_cast<uint16_t *>(a.order)[b] =
+                        static_cast<uint16_t>(pack_order<N, M>(ord));
+            }
         }
-        if (a.order) {
-            if (M == 4)
-                static_cast<uint8_t *>(a.order)[b] = static_cast<uint8_t>(pack_order<N, M>(ord));
-            else
-                static_cast<uint16_t *>(a.order)[b] =
-                    static_cast<uint16_t>(pack_order<N, M>(ord));
-        }
-    }
-    if (a.bits) {
-        if (M == 8) {
-            if (live) a.bits[b] = static_cast<uint8_t>(keep);
-        } else {
-            // two 4-bit masks per byte: the even lane of each pair stores both
-            // (every lane of the wave reaches the shuffle; dead lanes give 0)
-            const uint32_t hi = __shfl_xor(keep, 1);
-            if (live && !(b & 1)) a.bits[b >> 1] = static_cast<uint8_t>(keep | (hi << 4));
+        if (a.bits) {
+            if (M == 8) {
+                if (live) a.bits[b] = static_cast<uint8_t>(keep);
+            } else {
+                // two 4-bit masks per byte: the even lane of each pair stores both
+                // (every lane of the wave reaches the shuffle; dead lanes give 0)
+                const uint32_t hi = __shfl_xor(keep, 1);
+                if (live && !(b & 1)) a.bits[b >> 1] = static_cast<uint8_t>(keep | (hi << 4));
+            }
         }
     }
 }
@@ -234,9 +240,7 @@ __global__ __launch_bounds__(kThreads) void mp_fwd_kernel(MpArgs a) {
 // of one ulp of 1.  dpi = A * acc (+ dpi when accumulating).
 // ---------------------------------------------------------------------------
 template <int N, int M, bool ORDER_IN>
-__global__ __launch_bounds__(kThreads) void mp_bwd_kernel(MpArgs a) {
-    const int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    if (b >= a.nblocks) return;
+__device__ __forceinline__ void mp_bwd_block(const MpArgs &a, int64_t b) {
     float q[M];
     BlockIo<float, M>::load(a.pi, b, q);
     int ord[N];
@@ -289,15 +293,21 @@ __global__ __launch_bounds__(kThreads) void mp_bwd_kernel(MpArgs a) {
     BlockIo<float, M>::store(a.dpi, b, d);
 }
 
+template <int N, int M, bool ORDER_IN>
+__global__ __launch_bounds__(kThreads) void mp_bwd_kernel(MpArgs a) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    for (int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; b < a.nblocks;
+         b += stride)
+        mp_bwd_block<N, M, ORDER_IN>(a, b);
+}
+
 // ---------------------------------------------------------------------------
 // Initial logits: c at the kept positions of the initial mask, 0 elsewhere.
 // The mask is the packed prior (LSB-first, M bits per block) or the magnitude
 // top-N of w (N rounds of "first largest |w| not yet kept").
 // ---------------------------------------------------------------------------
 template <int N, int M, typename WT>
-__global__ __launch_bounds__(kThreads) void mp_init_kernel(MpInitArgs a) {
-    const int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    if (b >= a.nblocks) return;
+__device__ __forceinline__ void mp_init_block(const MpInitArgs &a, int64_t b) {
     uint32_t keep = 0;
     if (a.prior_bits) {
         if (M == 8)
@@ -328,8 +338,19 @@ __global__ __launch_bounds__(kThreads) void mp_init_kernel(MpInitArgs a) {
     BlockIo<float, M>::store(a.pi, b, v);
 }
 
+template <int N, int M, typename WT>
+__global__ __launch_bounds__(kThreads) void mp_init_kernel(MpInitArgs a) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    for (int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; b < a.nblocks;
+         b += stride)
+        mp_init_block<N, M, WT>(a, b);
+}
+
+// One thread per block up to 2^20 workgroups (2.7e8 blocks); larger tensors
+// loop, which keeps the grid inside its 32-bit dimension.
 unsigned blocks_for(int64_t nblocks) {
-    return static_cast<unsigned>((nblocks + kThreads - 1) / kThreads);
+    const int64_t want = (nblocks + kThreads - 1) / kThreads;
+    return static_cast<unsigned>(want < (INT64_C(1) << 20) ? want : (INT64_C(1) << 20));
 }
 
 template <int N, int M, typename WT>
