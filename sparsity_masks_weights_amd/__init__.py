@@ -376,6 +376,57 @@ def maskgs_debug_gumbel(words, g, stream=None):
 
 
 # --------------------------------------------------------------------------
+# autograd pairing of maskgs_fwd / maskgs_bwd
+# --------------------------------------------------------------------------
+def _masked_weight_function():
+    torch = _torch()
+
+    class MaskedWeight(torch.autograd.Function):
+        """W (.) M~ as a differentiable function of the logits z (MaskLLM
+        summary, section 3.4, Eqs. 5-8): the forward is maskgs_fwd, the
+        backward maskgs_bwd.  W is frozen (no gradient).  The backward adds the
+        regulariser term of -lambda * R to dz itself, so R is returned as a
+        non-differentiable side output (for logging) and must not also enter
+        the loss."""
+
+        @staticmethod
+        def forward(ctx, z, w, t, p, lam, save_y, out_dtype):
+            out = torch.empty(w.shape, dtype=out_dtype, device=w.device)
+            y = torch.empty_like(z) if save_y else None
+            reg = torch.zeros(1, dtype=torch.float64, device=w.device)
+            maskgs_fwd(t, p, w, z, out, y, reg)
+            ctx.save_for_backward(w, None if save_y else z, y)
+            ctx.t = t
+            ctx.p = SampleParams(p.seed, p.step, p.kappa, p.tau, p.flags)
+            ctx.lam = float(lam)
+            ctx.mark_non_differentiable(reg)
+            return out, reg
+
+        @staticmethod
+        def backward(ctx, dout, _dreg):
+            w, z, y = ctx.saved_tensors
+            dz = torch.empty_like(y if y is not None else z)
+            maskgs_bwd(ctx.t, ctx.p, w, z, y, dout.contiguous(), ctx.lam, dz)
+            return dz, None, None, None, None, None, None
+
+    return MaskedWeight
+
+
+_MaskedWeight = None
+
+
+def masked_weight(z, w, t: Tensor, p: SampleParams, lam: float = 0.0, save_y: bool = True,
+                  out_dtype=None):
+    """(W (.) M~, R) with autograd to z; see _masked_weight_function."""
+    global _MaskedWeight
+    torch = _torch()
+    if _MaskedWeight is None:
+        _MaskedWeight = _masked_weight_function()
+    return _MaskedWeight.apply(z, w, t, p, lam, save_y,
+                               torch.bfloat16 if out_dtype is None else out_dtype)
+
+
+# --------------------------------------------------------------------------
 # Linear-space mask learner (include/maskpro.h; MaskPro summary page,
 # "Approach" and "Limitations")
 # --------------------------------------------------------------------------

@@ -302,3 +302,30 @@ def test_fwd_hard_equals_fwd_then_extract(dev, mg, orc, case):
         assert np.array_equal(to_np(got), ref[name]), name
     h = orc.hard_extract(2, 4, to_np(z), rows, cols, w_raw=to_np(w))
     assert np.array_equal(to_np(bits), h["bits"]) and np.array_equal(to_np(vals), h["values"])
+
+
+@pytest.mark.parametrize("save_y", [True, False])
+def test_autograd_pairing_matches_the_abi_calls(mg, save_y):
+    """masked_weight (torch.autograd.Function over maskgs_fwd / maskgs_bwd)
+    gives exactly the outputs of the direct calls."""
+    import torch
+    rows, cols = 37, 72
+    B = rows * cols // 4
+    dev = torch.device("cuda:0")
+    w = _rand((rows, cols), 0.02, torch.bfloat16, dev, 90)
+    z0 = _rand((B, 6), 1.0, torch.float32, dev, 91)
+    G = _rand((rows, cols), 1e-3, torch.bfloat16, dev, 92)
+    t = mg.Tensor(2, 4, rows, cols, 5, 3)
+    p = mg.sample_params(11, 2, 100.0, 4.0)
+    z = z0.clone().requires_grad_(True)
+    out, reg = mg.masked_weight(z, w, t, p, lam=1e-5, save_y=save_y)
+    out.backward(G)
+    ref_out = torch.empty_like(w)
+    ref_reg = torch.zeros(1, dtype=torch.float64, device=w.device)
+    mg.maskgs_fwd(t, p, w, z0, ref_out, None, ref_reg)
+    ref_dz = torch.empty_like(z0)
+    mg.maskgs_bwd(t, p, w, z0, None, G, 1e-5, ref_dz)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out) and torch.equal(reg, ref_reg)
+    assert not reg.requires_grad
+    assert torch.equal(z.grad, ref_dz)
