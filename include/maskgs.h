@@ -55,8 +55,17 @@ extern "C" {
 #define MASKGS_E_HIP 7         /* the HIP runtime refused a launch                */
 #define MASKGS_E_CAPACITY 8    /* a host output buffer is too small               */
 
-/* Element types of weights, masked weights and upstream gradients. */
-typedef enum { MASKGS_F32 = 0, MASKGS_BF16 = 1 } maskgs_dtype;
+/* Element types of weights, masked weights and upstream gradients.  The two
+ * sentinels make every int32 value a valid maskgs_dtype for a C++
+ * implementation, so that an out-of-range code passed by a C caller is
+ * answered with MASKGS_E_DTYPE rather than being undefined; they are not
+ * element types. */
+typedef enum {
+    MASKGS_F32 = 0,
+    MASKGS_BF16 = 1,
+    MASKGS_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+    MASKGS_DTYPE_RANGE_MAX_ = 2147483647
+} maskgs_dtype;
 
 /* Sample flags. */
 #define MASKGS_NO_NOISE 1u /* g = 0 for every candidate (tests and diagnostics) */
