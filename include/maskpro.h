@@ -81,8 +81,10 @@ int maskpro_fwd(const maskgs_tensor_desc *t, const maskpro_draw_params *p, const
  *              maskpro_baseline).
  *   dpi        [B, M] fp32 output; accumulate != 0 adds to its contents.
  *              Must not alias pi.
- * fp32 arithmetic; each term is formed against the largest logit still in
- * play, so no exponent overflows or underflows whatever the spread. */
+ * fp32 arithmetic; each round is formed against the largest logit still in
+ * play, so its normaliser lies in [1, M] and no exponential overflows; terms
+ * that underflow to 0 are below 2^-126 of that round's largest.  Non-finite
+ * logits give non-finite gradients. */
 int maskpro_bwd(const maskgs_tensor_desc *t, const maskpro_draw_params *p, const float *pi,
                 const void *order, float advantage, float *dpi, int32_t accumulate,
                 hipStream_t stream);
