@@ -46,9 +46,11 @@ KERNEL_SOURCES = ["sparsity_masks_weights_amd/csrc/maskgs_k24.hip",
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama7b_all_linear")
+    ap.add_argument("--streams", type=int, default=2,
+                    help="worker streams the launches of a phase alternate between (1: in order)")
     ap.add_argument("--layers", type=int, default=None,
                     help="use only the first L layers (profiling runs; default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -56,7 +58,10 @@ def parse():
                     help="skip the training step with the fused AdamW update")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.streams < 1:
+        ap.error("--streams must be at least 1")
+    return args
 
 
 def source_hash() -> str:
@@ -90,7 +95,29 @@ def main():
     if args.layers is not None:
         specs = [t for t in specs if t.tensor_id < 7 * args.layers]
     stream = torch.cuda.current_stream()
-    sptr = ctypes.c_void_p(stream.cuda_stream)
+    # The launches of one phase alternate between worker streams (two by
+    # default, default priority), so that one tensor's kernel fills the CUs
+    # while the previous one drains (7B 2:4 step 40.7 -> 39.3 ms, 4:8 layer set
+    # 14.7 -> 14.0 ms; four streams gained less); every phase forks from and
+    # joins back to the main stream, where the step and phase events are
+    # recorded.  --streams 1 runs every launch in order on one stream.
+    workers = [torch.cuda.Stream(device=dev) for _ in range(args.streams)]
+    wptr = [ctypes.c_void_p(s.cuda_stream) for s in workers]
+
+    def sp(i):
+        return wptr[i % len(wptr)]
+
+    def fork():
+        e = torch.cuda.Event()
+        e.record(stream)
+        for s in workers:
+            s.wait_event(e)
+
+    def join():
+        for s in workers:
+            e = torch.cuda.Event()
+            e.record(s)
+            stream.wait_event(e)
 
     # ---- resident inputs and outputs --------------------------------------
     bufs = []
@@ -122,19 +149,19 @@ def main():
     fused = []
     params = [mg.SampleParams(0, 0, wl.kappa, wl.tau, 0)]
     pref = ctypes.byref(params[0])
-    for d in bufs:
+    for i, d in enumerate(bufs):
         dref = ctypes.byref(d["desc"])
         calls["fwd"].append((L.maskgs_fwd, (dref, pref, ptr(d["w"]), bf, ptr(d["z"]), ptr(d["out"]),
-                                            bf, ptr(d["y"]), ptr(reg), sptr)))
+                                            bf, ptr(d["y"]), ptr(reg), sp(i))))
         calls["bwd"].append((L.maskgs_bwd, (dref, pref, ptr(d["w"]), bf, None, ptr(d["y"]),
                                             ptr(d["G"]), gdt, ctypes.c_float(wl.lam), ptr(d["dz"]), 0,
-                                            sptr)))
+                                            sp(i))))
         calls["hard"].append((L.maskgs_hard_extract, (dref, ptr(d["z"]), ptr(d["w"]), bf, None,
                                                        ptr(d["bits"]), ptr(d["vals"]),
-                                                       ptr(d["vidx"]), sptr)))
+                                                       ptr(d["vidx"]), sp(i))))
         fused.append((L.maskgs_fwd_hard, (dref, pref, ptr(d["w"]), bf, ptr(d["z"]), ptr(d["out"]),
                                           bf, ptr(d["y"]), ptr(reg), None, ptr(d["bits"]),
-                                          ptr(d["vals"]), ptr(d["vidx"]), sptr)))
+                                          ptr(d["vals"]), ptr(d["vidx"]), sp(i))))
 
     # per-block algorithmic bytes of each kernel (bf16 weights, fp32 logits)
     K, M, N = wl.k, wl.m, wl.n
@@ -148,11 +175,11 @@ def main():
     }
     calls["fwd_hard"] = fused
     big = [i for i, d in enumerate(bufs) if d["B"] == max(x["B"] for x in bufs)]
-    # per-launch events bracket a sample of the largest tensors' launches (at
-    # most 8 per step, 40 over the default 5 steps): under rocprofv3 the event
-    # pairs around all 96 such launches of the 7B sweep left ~1 ms of gaps per
-    # step; without the profiler the step time is the same either way
-    big_set = set(big[::max(1, len(big) // 8)])
+    # per-launch events bracket one launch on a largest tensor per timed step,
+    # spread evenly over those tensors (step s times big[(s * stride) % len]):
+    # a timed launch runs alone, which costs the step the overlap on both sides
+    # of it
+    big_stride = max(1, len(big) // max(1, args.steps))
     # The step: the forward of every tensor with the hard mask of the same
     # logits fused in (one read of z and W), then the backward of every tensor.
     # Outputs are bit-identical to forward, backward, then extraction (z is not
@@ -165,25 +192,43 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    def step(kinds, timed_kind=None):
-        """One step.  Phase events bracket each kernel kind; per-launch events
-        are recorded only around the launches of `timed_kind` on the largest
-        tensors (the launch shape the roofline reports)."""
+    def step(kinds, timed_kind=None, step_no=0):
+        """One step (number step_no).  Phase events bracket each kernel kind;
+        per-launch events bracket one launch of `timed_kind` on a largest
+        tensor (the launch shape the roofline reports).  That launch runs
+        alone: it goes on the stream of the launch before it, which first
+        waits for the other workers' queued work, and they wait for it; so
+        its events time the kernel by itself and not its overlap with a
+        neighbour, and its start event directly follows a kernel in order."""
         reg.zero_()
+        nw = len(workers)
         for kind in kinds:
             p0, p1 = ev(), ev()
             p0.record(stream)
+            fork()
+            t = big[(step_no * big_stride) % len(big)] if kind == timed_kind else -1
             for i, (fn, a) in enumerate(calls[kind]):
-                rec = kind == timed_kind and i in big_set
-                if rec:
+                wi = (t - 1) % nw if i == t else i % nw
+                own = workers[wi]
+                others = [o for o in workers if o is not own]
+                if t >= 0 and i == max(t - 1, 0):
+                    for o in others:
+                        x = torch.cuda.Event()
+                        x.record(o)
+                        own.wait_event(x)
+                if i == t:
+                    a = a[:-1] + (wptr[wi],)     # the stream is the last argument
                     e0, e1 = ev(), ev()
-                    e0.record(stream)
+                    e0.record(own)
                 rc = fn(*a)
                 if rc != 0:
                     raise RuntimeError(f"{kind}: status {rc}")
-                if rec:
-                    e1.record(stream)
+                if i == t:
+                    e1.record(own)
+                    for o in others:
+                        o.wait_event(e1)
                     launch_ev[kind].append((e0, e1))
+            join()
             p1.record(stream)
             phase[kind].append((p0, p1))
 
@@ -202,12 +247,12 @@ def main():
     t0.record(stream)
     for s in range(args.steps):
         params[0].step = s
-        step(fused_kinds, dom)
+        step(fused_kinds, dom, s)
     t1.record(stream)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
 
-    # ---- per-kernel statistics (HIP events on the launch stream) ----------
+    # ---- per-kernel statistics (phase events on the main stream) ----------
     def kernel_stats(kinds, nsteps):
         out = {}
         for kind in kinds:
@@ -261,11 +306,13 @@ def main():
     pe0 = torch.cuda.Event(enable_timing=True)
     pe1 = torch.cuda.Event(enable_timing=True)
     pe0.record(stream)
-    for d in bufs:
+    fork()
+    for i, d in enumerate(bufs):
         rc = L.maskgs_prior_init(ctypes.byref(d["desc"]), ptr(d["z"]), None, ptr(d["w"]), bf,
-                                 ctypes.c_float(3.0), 0, sptr)
+                                 ctypes.c_float(3.0), 0, sp(i))
         if rc != 0:
             raise RuntimeError(f"prior_init: status {rc}")
+    join()
     pe1.record(stream)
     torch.cuda.synchronize()
     prior_ms = pe0.elapsed_time(pe1)
@@ -287,19 +334,19 @@ def main():
         }
         for mode, (fb, bb) in modes.items():
             seq = []
-            for d, v in zip(bufs, vbufs):
+            for i, (d, v) in enumerate(zip(bufs, vbufs)):
                 yp = ptr(d["y"]) if mode == "saved_y" else None
                 dref = ctypes.byref(d["desc"])
                 seq.append(("fwd_hard", L.maskgs_fwd_hard,
                             (dref, pref, ptr(d["w"]), bf, ptr(d["z"]), ptr(d["out"]), bf, yp,
                              ptr(reg), None, ptr(d["bits"]), ptr(d["vals"]), ptr(d["vidx"]),
-                             sptr)))
-            for d, v in zip(bufs, vbufs):
+                             sp(i))))
+            for i, (d, v) in enumerate(zip(bufs, vbufs)):
                 yp = ptr(d["y"]) if mode == "saved_y" else None
                 dref = ctypes.byref(d["desc"])
                 seq.append(("bwd_adamw", L.maskgs_bwd_adamw,
                             (dref, pref, ptr(d["w"]), bf, ptr(d["z"]), yp, ptr(d["G"]), gdt,
-                             ctypes.c_float(wl.lam), ptr(d["dz"]), ptr(v), hpref, sptr)))
+                             ctypes.c_float(wl.lam), ptr(d["dz"]), ptr(v), hpref, sp(i))))
             ph = {"fwd_hard": [], "bwd_adamw": []}
             t0, t1 = ev(), ev()
             torch.cuda.synchronize()
@@ -311,11 +358,13 @@ def main():
                 for kind in ("fwd_hard", "bwd_adamw"):
                     p0, p1 = ev(), ev()
                     p0.record(stream)
+                    fork()
                     for k_, fn, a in seq:
                         if k_ == kind:
                             rc = fn(*a)
                             if rc != 0:
                                 raise RuntimeError(f"{kind}: status {rc}")
+                    join()
                     p1.record(stream)
                     ph[kind].append((p0, p1))
             t1.record(stream)
@@ -338,12 +387,14 @@ def main():
     d0, d1 = ev(), ev()
     torch.cuda.synchronize()
     d0.record(stream)
-    for d in bufs:
+    fork()
+    for i, d in enumerate(bufs):
         rc = L.maskgs_mask_stats(ctypes.byref(d["desc"]), ptr(d["z"]), ctypes.c_float(wl.kappa),
                                  None, ptr(d["bits"]), ptr(d["w"]), bf, ptr(d["dz"]), ptr(st),
-                                 sptr)
+                                 sp(i))
         if rc != 0:
             raise RuntimeError(f"mask_stats: status {rc}")
+    join()
     d1.record(stream)
     torch.cuda.synchronize()
     stats_ms = d0.elapsed_time(d1)
@@ -369,17 +420,19 @@ def main():
         for kind in ("fwd_hard", "bwd"):
             p0, p1 = ev(), ev()
             p0.record(stream)
-            for d in bufs:
+            fork()
+            for i, d in enumerate(bufs):
                 dref = ctypes.byref(d["desc"])
                 if kind == "fwd_hard":
                     rc = L.maskgs_fwd_hard(dref, hsref, ptr(d["w"]), bf, ptr(d["z"]), ptr(d["out"]),
                                            bf, None, ptr(reg), None, ptr(d["bits"]),
-                                           ptr(d["vals"]), ptr(d["vidx"]), sptr)
+                                           ptr(d["vals"]), ptr(d["vidx"]), sp(i))
                 else:
                     rc = L.maskgs_bwd(dref, hsref, ptr(d["w"]), bf, ptr(d["z"]), None, ptr(d["G"]),
-                                      gdt, ctypes.c_float(wl.lam), ptr(d["dz"]), 0, sptr)
+                                      gdt, ctypes.c_float(wl.lam), ptr(d["dz"]), 0, sp(i))
                 if rc != 0:
                     raise RuntimeError(f"hard sample {kind}: status {rc}")
+            join()
             p1.record(stream)
             hs[kind].append((p0, p1))
     h1.record(stream)
@@ -435,17 +488,19 @@ def main():
             for kind in ("fwd", "bwd"):
                 p0, p1 = ev(), ev()
                 p0.record(stream)
-                for d, e in zip(bufs, mp_bufs):
+                fork()
+                for i, (d, e) in enumerate(zip(bufs, mp_bufs)):
                     dref = ctypes.byref(d["desc"])
                     op = ptr(e["order"]) if keep_order else None
                     if kind == "fwd":
                         rc = L.maskpro_fwd(dref, dpref, ptr(d["w"]), bf, ptr(e["pi"]),
-                                           ptr(d["out"]), bf, ptr(d["bits"]), op, sptr)
+                                           ptr(d["out"]), bf, ptr(d["bits"]), op, sp(i))
                     else:
                         rc = L.maskpro_bwd(dref, dpref, ptr(e["pi"]), op, adv, ptr(e["dpi"]), 0,
-                                           sptr)
+                                           sp(i))
                     if rc != 0:
                         raise RuntimeError(f"maskpro {kind}: status {rc}")
+                join()
                 p1.record(stream)
                 if s_ >= 0:
                     ph[kind].append((p0, p1))
@@ -498,7 +553,7 @@ def main():
                    "kappa": wl.kappa, "tau": wl.tau, "lambda": wl.lam,
                    "step": "fwd (y saved, reg) with the hard mask of the same logits fused in "
                            "(argmax, bit-pack, 2:4 compaction) + bwd (saved y)",
-                   "parallelism": "single GPU"},
+                   "streams": args.streams, "parallelism": "single GPU"},
         "fwd_bwd_blocks_per_s": round(total_blocks / (fwd_bwd_ms * 1e-3), 1),  # unfused fwd + bwd
         "fwd_bwd_hbm_gbs": round(fb_bytes * total_blocks / (fwd_bwd_ms * 1e-3) / 1e9, 1),
         "kernels": kstats,
