@@ -67,14 +67,12 @@ constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
 constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;
 constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
 
-// a ^ b ^ c, c uniform.  On gfx950 one v_bitop3_b32 (truth table 0x96 is the
-// three-input xor); the compiler forms it for some bit patterns but not for a
-// chained xor, which would cost two instructions per Philox output word.
+// a ^ b ^ c.  On gfx950 one v_bitop3_b32 (truth table 0x96 is the three-input
+// xor); the compiler forms it for some bit patterns but not for a chained xor,
+// which would cost two instructions per Philox output word.
 MASKGS_HD uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    uint32_t r;
-    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(c));
-    return r;
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
 #else
     return a ^ b ^ c;
 #endif

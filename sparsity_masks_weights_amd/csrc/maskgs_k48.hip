@@ -271,31 +271,32 @@ __device__ __forceinline__ void logits70(float (&v)[kK], uint64_t gb, const Geom
 // In place: a -> y = softmax(a) (Eq. 6).  Exponentials scaled by 2^64 so that
 // small soft-index values are rounded correctly instead of flushed.  With
 // SAMPLE, also returns the mask of the hard Gumbel-max sample, the candidate
-// of the first largest a_i: a_i - amax is +0 or -0 exactly there (the same
-// ordered key as argmax_key70, taken in the exponential's loop).
+// of the first largest a_i by the strict ">" scan of argmax_key70, taken in
+// the maximum's loop.
 template <bool SAMPLE = false>
 __device__ __forceinline__ void softmax70(float (&v)[kK], uint32_t *hard_mask = nullptr) {
     float amax = v[0];
+    float bv = v[0];
+    uint32_t best = C48::at(0);
 #pragma unroll
-    for (int i = 1; i < kK; ++i) amax = fmaxf(amax, v[i]);
+    for (int i = 1; i < kK; ++i) {
+        if (SAMPLE) {
+            const bool gt = v[i] > bv;
+            bv = gt ? v[i] : bv;
+            best = gt ? static_cast<uint32_t>(C48::at(i)) : best;
+        }
+        amax = fmaxf(amax, v[i]);
+    }
     float s = 0.0f;
-    uint32_t best = 0xFFFFFFFFu;
 #pragma unroll
     for (int i = 0; i < kK; ++i) {
-        const float d = v[i] - amax;
-        if (SAMPLE) {
-            const uint32_t nz = __float_as_uint(d) << 1;  // 0 iff a_i is the maximum
-            const uint32_t key = ((nz < 1u ? nz : 1u) << 15) | (static_cast<uint32_t>(i) << 8) |
-                                 C48::at(i);
-            best = best < key ? best : key;
-        }
-        v[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(d, 1.44269504088896341f, 64.0f));
+        v[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i] - amax, 1.44269504088896341f, 64.0f));
         s += v[i];
     }
     const float inv = __builtin_amdgcn_rcpf(s);
 #pragma unroll
     for (int i = 0; i < kK; ++i) v[i] *= inv;
-    if (SAMPLE) *hard_mask = best & 0xFFu;
+    if (SAMPLE) *hard_mask = best;
 }
 
 // Soft mask m_j = sum_i y_i S_ij (Eq. 7), candidates in table order.
@@ -310,25 +311,33 @@ __device__ __forceinline__ void soft_mask8(const float (&y)[kK], float (&m)[8]) 
 }
 
 // Hard mask of a block (section 3.4, Algorithm 1 inference step): the first
-// index of the largest logit, as a strict ">" scan from i = 0 finds it, and its
-// candidate mask.  Written without per-candidate compare masks: with zmax the
-// maximum, z_i - zmax is +0 or -0 exactly when z_i equals it (subnormals are
-// kept), and the key (not_max << 15) | (i << 8) | S_i is smallest for the
-// first such i.  Returns i << 8 | S_i.
+// index of the largest logit by a strict ">" scan from i = 0, and its
+// candidate mask.  A NaN never compares greater, so a NaN first logit, or a
+// block of NaN logits, keeps candidate 0; +inf is the largest value.  One
+// compare and two selects per candidate, in two independent chains (the
+// second half scanned from -inf, taken only if its maximum is strictly
+// larger, which is the same first maximum).  Returns i << 8 | S_i.
 template <typename Src>
 __device__ __forceinline__ uint32_t argmax_key70(const Src &v) {
-    float zmax = v[0];
+    constexpr int H = kK / 2;
+    float bv0 = v[0], bv1 = -__builtin_inff();
+    uint32_t best0 = C48::at(0), best1 = 0u;
 #pragma unroll
-    for (int i = 1; i < kK; ++i) zmax = fmaxf(zmax, v[i]);
-    uint32_t best = 0xFFFFFFFFu;
-#pragma unroll
-    for (int i = 0; i < kK; ++i) {
-        const uint32_t d = __float_as_uint(v[i] - zmax) << 1;   // 0 iff equal
-        const uint32_t key = ((d < 1u ? d : 1u) << 15) | (static_cast<uint32_t>(i) << 8) |
-                             C48::at(i);
-        best = best < key ? best : key;
+    for (int i = 1; i < H; ++i) {
+        const float x0 = v[i], x1 = v[H + i - 1];
+        const bool g0 = x0 > bv0, g1 = x1 > bv1;
+        bv0 = g0 ? x0 : bv0;
+        best0 = g0 ? ((static_cast<uint32_t>(i) << 8) | C48::at(i)) : best0;
+        bv1 = g1 ? x1 : bv1;
+        best1 = g1 ? ((static_cast<uint32_t>(H + i - 1) << 8) | C48::at(H + i - 1)) : best1;
     }
-    return best & 0x7FFFu;
+    {
+        const float x1 = v[kK - 1];
+        const bool g1 = x1 > bv1;
+        bv1 = g1 ? x1 : bv1;
+        best1 = g1 ? ((static_cast<uint32_t>(kK - 1) << 8) | C48::at(kK - 1)) : best1;
+    }
+    return bv1 > bv0 ? best1 : best0;
 }
 
 // The mask the forward applies: the soft mask y.S (Eq. 7) or the hard sample.
