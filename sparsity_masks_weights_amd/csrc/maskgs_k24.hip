@@ -403,33 +403,42 @@ __device__ __forceinline__ void hard_pair(uint8_t *idx, uint8_t *bits, void *val
     if (values) Io<WT>::store_values(values, p, two, d, lh0, lh1);
 }
 
-// Soft index of a pair (section 3.4, Eq. 6 and Algorithm 1 steps 1-2):
-// a_i = fp32(fp32(kappa z_i + g_i) * fp32(1/tau)) with g the contract noise.
-// The noise flag is uniform, so the twelve Gumbel evaluations form one
-// straight-line block the scheduler can interleave.
+// Gumbel noise of a pair (section 3.4, Eq. 5): g_i of the contract for its
+// twelve candidates, +0 with the noise switched off.  It depends only on the
+// counters, so the kernels draw it right after requesting the pair's loads and
+// the memory latency passes under the noise arithmetic.  The noise flag is
+// uniform, so the twelve Gumbel evaluations form one straight-line block the
+// scheduler can interleave.
 template <int PHASE>
-__device__ __forceinline__ void pair_logits(const Geometry &g, const Noise &nz, int64_t p,
-                                            const float (&z)[12], float (&a12)[12]) {
+__device__ __forceinline__ void pair_noise(const Geometry &g, const Noise &nz, int64_t p,
+                                           float (&g12)[12]) {
     if (nz.no_noise) {
 #pragma unroll
-        for (int i = 0; i < 12; ++i) a12[i] = __builtin_fmaf(nz.kappa, z[i], 0.0f) * nz.tau_inv;
+        for (int i = 0; i < 12; ++i) g12[i] = 0.0f;
     } else {
         uint32_t wd[12];
         pair_words<PHASE>(g, nz, p, wd);
 #pragma unroll
-        for (int i = 0; i < 12; ++i)
-            a12[i] = __builtin_fmaf(nz.kappa, z[i], -neg_gumbel(wd[i])) * nz.tau_inv;
+        for (int i = 0; i < 12; ++i) g12[i] = -neg_gumbel(wd[i]);
     }
 }
 
-// Soft index of a pair and, under the hard-sample flag, the masks of its two
-// Gumbel-max samples S[first argmax a] (0 otherwise).
-template <int PHASE>
-__device__ __forceinline__ void pair_sample(const Geometry &g, const Noise &nz, int64_t p,
-                                            const float (&z)[12], float (&y)[12],
+// Perturbed logits of a pair (section 3.4, Eq. 6 and Algorithm 1 steps 1-2):
+// a_i = fp32(fp32(kappa z_i + g_i) * fp32(1/tau)).
+__device__ __forceinline__ void pair_logits(const Noise &nz, const float (&z)[12],
+                                            const float (&g12)[12], float (&a12)[12]) {
+#pragma unroll
+    for (int i = 0; i < 12; ++i) a12[i] = __builtin_fmaf(nz.kappa, z[i], g12[i]) * nz.tau_inv;
+}
+
+// Soft index of a pair from its logits and noise and, under the hard-sample
+// flag, the masks of its two Gumbel-max samples S[first argmax a] (0
+// otherwise).
+__device__ __forceinline__ void pair_sample(const Noise &nz, const float (&z)[12],
+                                            const float (&g12)[12], float (&y)[12],
                                             uint32_t (&hm)[2]) {
     float a12[12];
-    pair_logits<PHASE>(g, nz, p, z, a12);
+    pair_logits(nz, z, g12, a12);
     hm[0] = hm[1] = 0u;
     if (nz.hard_sample) {
         hm[0] = cand_mask6(first_argmax6(a12));
@@ -487,12 +496,14 @@ __global__ __launch_bounds__(kThreads) void fwd24_kernel(FwdArgs a) {
             uint32_t wd[8];
             Io<WT>::load8(a.w, p, two, w, wd);
             load12(a.z, p, two, z);
+            float g12[12];
+            pair_noise<PHASE>(a.g, a.nz, p, g12);
             if (hard) {
                 // hard mask of the same logits (argmax of z, not of the sample)
                 hard_pair<WT>(a.idx, a.bits, a.values, a.val_idx, p, two, z, wd);
             }
             uint32_t hm[2];
-            pair_sample<PHASE>(a.g, a.nz, p, z, y, hm);
+            pair_sample(a.nz, z, g12, y, hm);
             float racc = 0.0f;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -537,9 +548,10 @@ __global__ __launch_bounds__(kThreads) void bwd24_kernel(BwdArgs a) {
             if (SAVED) {
                 load12(a.y, p, two, y);
             } else {
-                float z[12];
+                float z[12], g12[12];
                 load12(a.z, p, two, z);
-                pair_sample<PHASE>(a.g, a.nz, p, z, y, hm);
+                pair_noise<PHASE>(a.g, a.nz, p, g12);
+                pair_sample(a.nz, z, g12, y, hm);
             }
             float prev[12];
             if (a.accumulate) load12(a.dz, p, two, prev);
@@ -621,9 +633,10 @@ __global__ __launch_bounds__(kThreads) void reg24_kernel(RegArgs a) {
         if (SAVED) {
             load12(a.y, p, two, y);
         } else {
-            float z[12];
+            float z[12], g12[12];
             load12(a.z, p, two, z);
-            pair_sample<PHASE>(a.g, a.nz, p, z, y, hm);
+            pair_noise<PHASE>(a.g, a.nz, p, g12);
+            pair_sample(a.nz, z, g12, y, hm);
         }
         float racc = 0.0f;
 #pragma unroll
@@ -819,8 +832,9 @@ __global__ __launch_bounds__(kThreads) void stats24_kernel(StatsArgs a) {
         if (a.ref_bits) rb = a.ref_bits[p];
         int k0, k1;
         if (SAMPLED) {
-            float a12[12];
-            pair_logits<PHASE>(a.g, a.nz, p, z, a12);
+            float a12[12], g12[12];
+            pair_noise<PHASE>(a.g, a.nz, p, g12);
+            pair_logits(a.nz, z, g12, a12);
             k0 = first_argmax6(a12);
             k1 = first_argmax6(a12 + 6);
         } else {
