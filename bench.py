@@ -533,6 +533,7 @@ def main():
 
     fwd_bwd_ms = ustats["fwd"]["ms_per_step"] + ustats["bwd"]["ms_per_step"]
     fb_bytes = per_block_bytes["fwd"] + per_block_bytes["bwd"]
+    step_bytes = sum(per_block_bytes[k] for k in fused_kinds) * total_blocks
     result = {
         "metric": (f"weight-blocks/s and HBM GB/s (% of peak), {wl.n}:{wl.m} mask fwd+bwd, "
                    f"{'LLaMA-2-7B' if wl.key.startswith('llama') else 'Nemotron-4-15B'} shapes"),
@@ -554,6 +555,10 @@ def main():
                    "step": "fwd (y saved, reg) with the hard mask of the same logits fused in "
                            "(argmax, bit-pack, 2:4 compaction) + bwd (saved y)",
                    "streams": args.streams, "parallelism": "single GPU"},
+        # the whole timed step as one memory stream: its algorithmic bytes (every
+        # kernel of the step, every tensor) over the step time
+        "step_hbm_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "fwd_bwd_blocks_per_s": round(total_blocks / (fwd_bwd_ms * 1e-3), 1),  # unfused fwd + bwd
         "fwd_bwd_hbm_gbs": round(fb_bytes * total_blocks / (fwd_bwd_ms * 1e-3) / 1e9, 1),
         "kernels": kstats,
