@@ -20,7 +20,9 @@
  *   Support.  N:M = 2:4 (K = 6) and 4:8 (K = 70) on the GPU.
  *   Memory.   Every array argument is device memory owned by the caller, except
  *             where a comment says "host".  The library allocates nothing and
- *             keeps no mutable state between calls; calls are thread safe.
+ *             keeps no state between calls that affects results (only a cache
+ *             of each device's compute-unit count, for launch sizes); calls
+ *             are thread safe.
  *             Every device pointer must be 16-byte aligned.  Outputs must not
  *             alias inputs except where stated (prior_init updates z in place,
  *             bwd with accumulate reads and writes dz).

@@ -4,11 +4,13 @@
 //   weights   8 bf16 = one 16 B load (fp32: two),   logits 12 fp32 = three 16 B loads,
 //   and the pair's 12 noise words come from 3 Philox calls when the pair starts
 //   at an even global block (4 calls otherwise; PHASE is uniform per launch).
-// A workgroup walks tiles of 256 consecutive pairs (grid-stride, the same trip
-// count for every lane).  Inputs are read directly (lanes 48 B apart, three
-// 16 B loads each); 48-byte-per-lane outputs (soft index, logit gradient,
-// seeded logits) are transposed through LDS so that every global store is a
-// fully coalesced, non-temporal 16 B-per-lane stream.
+// A workgroup walks tiles of kThreads consecutive pairs (grid-stride, the same
+// trip count for every lane).  Inputs are read directly (lanes 48 B apart,
+// three 16 B loads each), and the pair's noise, which depends only on the
+// counters, is drawn while those loads are in flight; 48-byte-per-lane outputs
+// (soft index, logit gradient, seeded logits) are transposed through LDS so
+// that every global store is a fully coalesced, non-temporal 16 B-per-lane
+// stream.
 // The path is an HBM/VALU streaming path: no matrix cores are involved.
 #include <hip/hip_runtime.h>
 
@@ -25,7 +27,7 @@ constexpr int kThreads = MASKGS_K24_THREADS;
 #ifndef MASKGS_K24_WG_PER_CU
 #define MASKGS_K24_WG_PER_CU 8
 #endif
-constexpr int kWavesPerCU = MASKGS_K24_WG_PER_CU;  // grid cap: workgroups of 256 per CU
+constexpr int kWgPerCU = MASKGS_K24_WG_PER_CU;  // grid cap: workgroups of kThreads lanes per CU
 using C24 = Cands<2, 4>;
 
 // ---------------------------------------------------------------------------
@@ -871,7 +873,7 @@ __global__ __launch_bounds__(kThreads) void stats24_kernel(StatsArgs a) {
 
 template <typename K, typename A>
 hipError_t go(K kernel, const A &args, int64_t items, hipStream_t s,
-              int wg_per_cu = kWavesPerCU) {
+              int wg_per_cu = kWgPerCU) {
     const unsigned grid = grid_for(items, kThreads, wg_per_cu);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, s, args);
     return hipGetLastError();
