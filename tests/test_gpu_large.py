@@ -6,7 +6,9 @@ Every index and byte offset past 2^31 must be carried in 64 bits: the
 forward with the hard mask fused in and the backward run on the whole tensor
 in the benchmark's launch configuration, and the oracle checks the first,
 middle and last rows (noise keyed on their global block indices), the hard
-mask of those rows, and the backward.  About 32 GB of device memory.
+mask of those rows, and the backward; likewise the linear-space draw and
+policy gradient on [B, M] logits past 2^31 floats.  At most 36 GB of device
+memory per test.
 """
 import math
 
@@ -74,4 +76,44 @@ def test_logit_arrays_past_2_31(mg, orc, case):
         d = orc.bwd(n, m, wn, zn, widen(to_np(G[r:r + 1])), lam=lam, **kw)
         assert_close(to_np(dz[b0:b1]), d, f"{what} dz")
     del w, G, z, out, y, dz, idx, bits
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("nm", [(2, 4), (4, 8)])
+def test_linear_space_logits_past_2_31(mg, orc, nm):
+    """The linear-space draw and policy gradient on a tensor whose [B, M]
+    logits hold more than 2^31 floats (2:4: 32768 x 65568 weights, 537M
+    blocks; 4:8: 16384 x 131104, 268M blocks), first, middle and last rows
+    against the oracle."""
+    import torch
+    from test_gpu_maskpro import _order_tensor, assert_pg, order_np, pack_order
+    n, m = nm
+    rows, cols = (32768, 65568) if m == 4 else (16384, 131104)
+    bpr = cols // m
+    B = rows * bpr
+    assert B * m > 2**31
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(cols + m)
+    w = (torch.randn(rows, cols, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    pi = torch.randn(B, m, generator=g, device=dev)
+    t = mg.Tensor(n, m, rows, cols, 0, 4)
+    p = mg.draw_params(77, 5)
+    out = torch.empty_like(w)
+    order = _order_tensor(B, m, dev)
+    mg.maskpro_fwd(t, p, pi, w, out, order=order)
+    dpi = torch.empty_like(pi)
+    adv = -0.4
+    mg.maskpro_bwd(t, p, pi, adv, dpi, order=order)
+    torch.cuda.synchronize()
+    for r in (0, rows // 2, rows - 1):
+        b0, b1 = r * bpr, (r + 1) * bpr
+        pin = to_np(pi[b0:b1])
+        kw = dict(seed=p.seed, step=p.step, tensor_id=4, block_offset=b0)
+        f = orc.maskpro_fwd(n, m, widen(to_np(w[r:r + 1])), pin, **kw)
+        assert np.array_equal(order_np(order[b0:b1], m), pack_order(f["order"], m)), r
+        assert np.array_equal(to_np(out[r:r + 1]), f["out"]), r
+        ref = orc.maskpro_grad(n, m, pin, 1, cols, advantage=adv, order=f["order"])
+        assert_pg(to_np(dpi[b0:b1]), ref, adv, n, f"{n}:{m} row {r}")
+    del w, pi, out, order, dpi
     torch.cuda.empty_cache()
