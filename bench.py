@@ -15,7 +15,9 @@ reported under `train_step` (--no-train-step skips it), and one pass of the
 training diagnostics (maskgs_mask_stats) over every tensor under `diagnostics`,
 and the step with the hard Gumbel-max sample (straight-through backward) under
 `hard_sample_step`, and the step of the linear-space variant (M logits per
-block, Gumbel-top-k draw, policy gradient) under `linear_space_step`.
+block, Gumbel-top-k draw, policy gradient) under `linear_space_step`.  Within
+each phase the per-tensor launches alternate between two HIP streams
+(--streams), so one tensor's kernel fills the GPU while the previous drains.
 
 Prints ONE JSON line.  `value` = 2:4 weight blocks per second through the whole
 step; `roofline` describes the kernel with the largest share of the step;
