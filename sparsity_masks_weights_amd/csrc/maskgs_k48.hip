@@ -3,7 +3,7 @@
 // Work item = one block per lane (70 candidates, K = C(8,4)); a workgroup is
 // one wave and walks tiles of 64 consecutive blocks.  Logit-sized streams
 // (280 B per block) always cross HBM as fully coalesced 16 B-per-lane copies
-// through LDS.  Two kernel shapes:
+// through LDS (stores non-temporal).  Two kernel shapes:
 //  - noise kernels (forward; backward and regulariser that recompute the soft
 //    index) are VALU-bound: the 70 values of a block live in registers and the
 //    LDS stage holds 32 blocks (8960 B) at a time;
@@ -30,6 +30,13 @@ namespace maskgs {
 namespace {
 
 constexpr int kWave = 64;
+typedef float v4f48 __attribute__((ext_vector_type(4)));
+
+// Non-temporal 16-byte store: the logit-sized outputs (soft index, gradient,
+// seeded logits) are written once and not read again by the kernel.
+__device__ __forceinline__ void nt_store4(float4 *p, float4 v) {
+    __builtin_nontemporal_store(v4f48{v.x, v.y, v.z, v.w}, reinterpret_cast<v4f48 *>(p));
+}
 constexpr int kK = 70;
 constexpr int kHalf = 32;  // blocks staged per LDS round
 constexpr int kWgPerCU = 16;
@@ -102,7 +109,7 @@ struct TileRegs {
 #pragma unroll
         for (int k = 0; k < kRounds; ++k) {
             const int i = k * kWave + lane;
-            if (i < n4) reinterpret_cast<float4 *>(dst)[i] = v[k];
+            if (i < n4) nt_store4(reinterpret_cast<float4 *>(dst) + i, v[k]);
         }
         if ((nf & 3) && lane == 0) reinterpret_cast<float2 *>(dst)[2 * n4] = tail;
     }
@@ -153,7 +160,7 @@ __device__ __forceinline__ void tile_out(float *g, int64_t b0, int nb, float *st
         float *dst = g + (b0 + h * kHalf) * kK;
         const int nf = cnt * kK, n4 = nf >> 2;
         for (int i = lane; i < n4; i += kWave)
-            reinterpret_cast<float4 *>(dst)[i] = reinterpret_cast<const float4 *>(stage)[i];
+            nt_store4(reinterpret_cast<float4 *>(dst) + i, reinterpret_cast<const float4 *>(stage)[i]);
         if ((nf & 3) && lane == 0)
             reinterpret_cast<float2 *>(dst)[2 * n4] = reinterpret_cast<const float2 *>(stage)[2 * n4];
         __syncthreads();
