@@ -28,6 +28,13 @@ constexpr int kThreads = MASKGS_K24_THREADS;
 #define MASKGS_K24_WG_PER_CU 8
 #endif
 constexpr int kWgPerCU = MASKGS_K24_WG_PER_CU;  // grid cap: workgroups of kThreads lanes per CU
+// The cap of the kernels without noise or end-of-workgroup atomics (hard
+// extract, prior seeding, the backward fused with AdamW): a grid well past the
+// resident set keeps each workgroup's share, and so the launch's tail, short.
+// Measured on the 7B sweep against the cap of 8: hard extract 11.4 -> 10.7 ms,
+// prior seeding 16.8 -> 15.8 ms, training backward 46.8 -> 45.6 ms; the
+// forward and the plain backward measured best at 8.
+constexpr int kWgPerCUStream = 64;
 using C24 = Cands<2, 4>;
 
 // ---------------------------------------------------------------------------
@@ -903,13 +910,14 @@ hipError_t fwd24_dispatch(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype o_dt
 template <int PHASE, bool SAVED, bool ADAMW>
 hipError_t bwd24_dispatch(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, hipStream_t s) {
     const int64_t np = (a.g.nblocks + 1) >> 1;
+    const int c = ADAMW ? kWgPerCUStream : kWgPerCU;
     if (w_dt == MASKGS_BF16 && g_dt == MASKGS_BF16)
-        return go(bwd24_kernel<PHASE, bf16_t, bf16_t, SAVED, ADAMW>, a, np, s);
+        return go(bwd24_kernel<PHASE, bf16_t, bf16_t, SAVED, ADAMW>, a, np, s, c);
     if (w_dt == MASKGS_BF16)
-        return go(bwd24_kernel<PHASE, bf16_t, float, SAVED, ADAMW>, a, np, s);
+        return go(bwd24_kernel<PHASE, bf16_t, float, SAVED, ADAMW>, a, np, s, c);
     if (g_dt == MASKGS_BF16)
-        return go(bwd24_kernel<PHASE, float, bf16_t, SAVED, ADAMW>, a, np, s);
-    return go(bwd24_kernel<PHASE, float, float, SAVED, ADAMW>, a, np, s);
+        return go(bwd24_kernel<PHASE, float, bf16_t, SAVED, ADAMW>, a, np, s, c);
+    return go(bwd24_kernel<PHASE, float, float, SAVED, ADAMW>, a, np, s, c);
 }
 
 template <bool ADAMW>
@@ -947,15 +955,16 @@ hipError_t launch_reg24(const RegArgs &a, maskgs_dtype w_dt, hipStream_t s) {
 
 hipError_t launch_hard24(const HardArgs &a, maskgs_dtype w_dt, hipStream_t s) {
     const int64_t np = (a.g.nblocks + 1) >> 1;
-    if (a.values && w_dt == MASKGS_F32) return go(hard24_kernel<float>, a, np, s);
-    return go(hard24_kernel<bf16_t>, a, np, s);
+    if (a.values && w_dt == MASKGS_F32) return go(hard24_kernel<float>, a, np, s, kWgPerCUStream);
+    return go(hard24_kernel<bf16_t>, a, np, s, kWgPerCUStream);
 }
 
 hipError_t launch_prior24(const PriorArgs &a, maskgs_dtype w_dt, hipStream_t s) {
     const int64_t np = (a.g.nblocks + 1) >> 1;
-    if (a.prior_bits) return go(prior24_kernel<bf16_t, true>, a, np, s);
-    if (w_dt == MASKGS_F32) return go(prior24_kernel<float, false>, a, np, s);
-    return go(prior24_kernel<bf16_t, false>, a, np, s);
+    const int c = kWgPerCUStream;
+    if (a.prior_bits) return go(prior24_kernel<bf16_t, true>, a, np, s, c);
+    if (w_dt == MASKGS_F32) return go(prior24_kernel<float, false>, a, np, s, c);
+    return go(prior24_kernel<bf16_t, false>, a, np, s, c);
 }
 
 template <int PHASE>
