@@ -84,6 +84,8 @@ CASES = [
     (4, 8, 37, 72, "bf16", 3, 4, 11, 2, 100.0, 2.0, 1, True),    # 333 blocks: ragged tile
     (4, 8, 16, 128, "f32", 0, 0, 0, 0, 100.0, 2.0, 4, False),
     (4, 8, 130, 64, "bf16", 2, 3, 5, 1, 10.0, 8.0, 9, True),
+    (2, 4, 37, 72, "bf16", 2**56 - 333, 7, 2**40, 3, 100.0, 4.0, 2, False),  # high counters
+    (4, 8, 37, 72, "bf16", 2**56 - 333, 7, 2**40, 3, 100.0, 2.0, 2, False),
 ]
 
 

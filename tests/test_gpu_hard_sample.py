@@ -41,6 +41,8 @@ CASES = [
     (2, 4, 37, 72, "f32", "f32", 5, 3, 11, 2, 1.0, 2.0),      # noise-dominated, odd offset
     (4, 8, 37, 72, "bf16", "bf16", 3, 4, 11, 2, 100.0, 2.0),  # ragged tile
     (4, 8, 16, 128, "f32", "f32", 1, 1, 7, 5, 10.0, 0.5),
+    (2, 4, 37, 72, "bf16", "bf16", 2**56 - 333, 2, 2**63 + 1, 9, 10.0, 2.0),  # high counters
+    (4, 8, 37, 72, "bf16", "bf16", 2**56 - 333, 2, 2**63 + 1, 9, 10.0, 2.0),
 ]
 
 

@@ -129,6 +129,9 @@ CASES = [
     (300, 512, "bf16", 2, 224, 1, 9, 250.0, 1.0, 0.01),  # small logits, many workgroups
     (1, 4, "f32", 0, 0, 0, 0, 100.0, 4.0, 1.0),          # a single block
     (3, 8, "f32", 1, 0, 0, 0, 100.0, 4.0, 1.0),
+    # global blocks near the 2^56 limit: Philox counters with a non-zero high word
+    (37, 36, "bf16", 2**56 - 333, 6, 2**63 + 5, 2**32 - 1, 100.0, 4.0, 1.0),   # odd
+    (64, 1024, "f32", 2**55 + 2, 13, 1, 1, 100.0, 4.0, 1.0),                # even
 ]
 
 

@@ -42,6 +42,9 @@ CASES = [
     (5, 8, "f32", 1, 1, 2, 0, 100.0, 2.0),        # 5 blocks
     (64, 512, "f32", 12345, 9, 2**33 + 1, 7, 500.0, 0.05),
     (130, 64, "bf16", 2, 3, 5, 1, 10.0, 8.0),
+    # global blocks near the 2^56 limit: Philox counters with a non-zero high word
+    (37, 72, "bf16", 2**56 - 333, 5, 2**64 - 1, 2**32 - 1, 100.0, 2.0),     # odd
+    (16, 128, "f32", 2**48 + 6, 6, 3, 1, 100.0, 2.0),                      # even
 ]
 
 
