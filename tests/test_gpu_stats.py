@@ -49,6 +49,8 @@ CASES = [
     (2, 4, 41, 20, "bf16", 1, 1, 1e5, 0.05),         # near one-hot, sampled
     (4, 8, 37, 72, "bf16", 3, 4, 100.0, None),       # 333 blocks: ragged tile
     (4, 8, 130, 64, "f32", 2, 2, 10.0, 2.0),         # sampled
+    (2, 4, 37, 72, "f32", 2**56 - 333, 5, 1.0, 4.0),  # sampled, Philox counters' high word
+    (4, 8, 37, 72, "bf16", 2**56 - 333, 6, 10.0, 2.0),
 ]
 
 
