@@ -30,7 +30,10 @@
  *             runs asynchronously; faults surface at the caller's synchronise.
  *   Errors.   Each call returns MASKGS_OK (0) or a MASKGS_E_* status.  All
  *             argument checks run on the host before anything is enqueued: on
- *             an error status nothing has been launched.  Data-dependent
+ *             an error status nothing has been launched.  The descriptor, the
+ *             scalars and the combination of arguments are checked first; a
+ *             tensor with no blocks (rows or cols 0) then returns MASKGS_OK
+ *             without reading or checking any array pointer.  Data-dependent
  *             conditions (NaN logits, priors matching no candidate) are not
  *             errors; their behaviour is stated per entry point.
  */
@@ -49,8 +52,10 @@ extern "C" {
 /* Status codes. */
 #define MASKGS_OK 0
 #define MASKGS_E_NULL 1        /* a required pointer is NULL                      */
-#define MASKGS_E_SHAPE 2       /* rows/cols negative, or cols % M != 0            */
-#define MASKGS_E_UNSUPPORTED 3 /* N:M other than 2:4 / 4:8, or 2:4-only output    */
+#define MASKGS_E_SHAPE 2       /* rows/cols negative, cols % M != 0, or past the
+                                  size limits of maskgs_tensor_desc             */
+#define MASKGS_E_UNSUPPORTED 3 /* N:M other than 2:4 / 4:8, a 2:4-only output, or
+                                  a saved y under MASKGS_HARD_SAMPLE            */
 #define MASKGS_E_DTYPE 4       /* dtype code out of range                         */
 #define MASKGS_E_ALIGN 5       /* a device pointer is not 16-byte aligned         */
 #define MASKGS_E_RANGE 6       /* kappa<=0, tau<=0, lambda<0, alpha<0, non-finite, bad mode */
@@ -83,7 +88,9 @@ typedef enum {
  * of the first block described: the noise of a block depends on its global
  * index, so a tensor split into row ranges with matching offsets draws exactly
  * the noise of the whole tensor.  tensor_id separates the noise streams of the
- * layers of a model. */
+ * layers of a model.  Limits (MASKGS_E_SHAPE beyond them): block_offset at most
+ * 2^56, and rows * (cols/m) * 80 at most 2^56, so that every element index and
+ * Philox word index fits 64 bits. */
 typedef struct {
     int32_t n, m;          /* N:M pattern: keep n of every m weights             */
     int64_t rows, cols;    /* weight shape [rows, cols]                          */

@@ -89,7 +89,7 @@ const char *maskgs_status_str(int status) {
         case MASKGS_OK: return "ok";
         case MASKGS_E_NULL: return "a required pointer is NULL";
         case MASKGS_E_SHAPE: return "invalid shape (negative size, cols not a multiple of M, or too large)";
-        case MASKGS_E_UNSUPPORTED: return "unsupported N:M pattern or output for this pattern";
+        case MASKGS_E_UNSUPPORTED: return "unsupported N:M pattern, output for this pattern, or argument combination";
         case MASKGS_E_DTYPE: return "invalid dtype code";
         case MASKGS_E_ALIGN: return "a device pointer is not 16-byte aligned";
         case MASKGS_E_RANGE: return "scalar argument out of range (kappa, tau > 0; lambda, alpha >= 0; finite; mode 0/1)";
@@ -168,8 +168,8 @@ int maskgs_bwd(const maskgs_tensor_desc *t, const maskgs_sample_params *p, const
     if (rc) return rc;
     if ((rc = check_params(p, &nz))) return rc;
     if (!std::isfinite(lambda) || lambda < 0.0f) return MASKGS_E_RANGE;
-    if (g.nblocks == 0) return MASKGS_OK;
     if (nz.hard_sample && y_saved) return MASKGS_E_UNSUPPORTED;
+    if (g.nblocks == 0) return MASKGS_OK;
     if (!w || !dout || !dz || (!z && !y_saved)) return MASKGS_E_NULL;
     if (!valid_dtype(w_dt) || !valid_dtype(dout_dt)) return MASKGS_E_DTYPE;
     if (misaligned(w) || misaligned(z) || misaligned(y_saved) || misaligned(dout) ||
@@ -254,8 +254,8 @@ int maskgs_reg_reduce(const maskgs_tensor_desc *t, const maskgs_sample_params *p
     int rc = check_desc(t, &g);
     if (rc) return rc;
     if ((rc = check_params(p, &nz))) return rc;
-    if (g.nblocks == 0) return MASKGS_OK;
     if (nz.hard_sample && y_saved) return MASKGS_E_UNSUPPORTED;
+    if (g.nblocks == 0) return MASKGS_OK;
     if (!w || !reg_accum || (!z && !y_saved)) return MASKGS_E_NULL;
     if (!valid_dtype(w_dt)) return MASKGS_E_DTYPE;
     if (misaligned(w) || misaligned(z) || misaligned(y_saved) || misaligned(reg_accum))

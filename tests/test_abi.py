@@ -59,6 +59,16 @@ def test_fwd_validation(L):
     assert _fwd(L, desc=mg.TensorDesc(3, 8, 8, 16, 0, 0)) == mg.MASKGS_E_UNSUPPORTED
     assert _fwd(L, desc=mg.TensorDesc(2, 4, 8, 18, 0, 0)) == mg.MASKGS_E_SHAPE
     assert _fwd(L, desc=mg.TensorDesc(2, 4, -1, 16, 0, 0)) == mg.MASKGS_E_SHAPE
+    # size limits: rows * (cols/m) * 80 and block_offset at most 2^56 (checked
+    # before the empty-tensor return, so the empty tensors below launch nothing)
+    for m_, cols in ((4, 16), (8, 1024)):
+        bpr = cols // m_
+        top = (1 << 56) // (bpr * 80)
+        n_ = 2 if m_ == 4 else 4
+        assert _fwd(L, desc=mg.TensorDesc(n_, m_, top + 1, cols, 0, 0)) == mg.MASKGS_E_SHAPE
+    assert _fwd(L, desc=mg.TensorDesc(2, 4, 0, 16, 1 << 56, 0)) == mg.MASKGS_OK
+    assert _fwd(L, desc=mg.TensorDesc(2, 4, 0, 16, (1 << 56) + 1, 0)) == mg.MASKGS_E_SHAPE
+    assert _fwd(L, desc=mg.TensorDesc(4, 8, 0, 16, 2**64 - 1, 0)) == mg.MASKGS_E_SHAPE
     assert _fwd(L, params=mg.SampleParams(0, 0, 100.0, 0.0, 0)) == mg.MASKGS_E_RANGE
     assert _fwd(L, params=mg.SampleParams(0, 0, -1.0, 1.0, 0)) == mg.MASKGS_E_RANGE
     assert _fwd(L, params=mg.SampleParams(0, 0, float("nan"), 1.0, 0)) == mg.MASKGS_E_RANGE
@@ -158,6 +168,14 @@ def test_hard_sample_needs_recomputed_soft_index(L):
     opt = mg.AdamWParams(5e-4, 0.9, 0.999, 1e-8, 0.1, 1)
     assert L.maskgs_bwd_adamw(bd, bp, A, 1, A, A, A, 1, 1e-5, A, A, ctypes.byref(opt),
                               None) == mg.MASKGS_E_UNSUPPORTED
+    # the combination is refused before the empty-tensor return, as every
+    # argument check is
+    e = ctypes.byref(mg.TensorDesc(2, 4, 0, 16, 0, 0))
+    assert L.maskgs_bwd(e, bp, A, 1, A, A, A, 1, 1e-5, A, 0, None) == mg.MASKGS_E_UNSUPPORTED
+    assert L.maskgs_reg_reduce(e, bp, A, 1, A, A, A, None) == mg.MASKGS_E_UNSUPPORTED
+    assert L.maskgs_bwd_adamw(e, bp, A, 1, A, A, A, 1, 1e-5, A, A, ctypes.byref(opt),
+                              None) == mg.MASKGS_E_UNSUPPORTED
+    assert L.maskgs_bwd(e, bp, A, 1, A, None, A, 1, 1e-5, A, 0, None) == mg.MASKGS_OK
 
 
 def test_maskpro_validation(L):
