@@ -33,7 +33,8 @@
  *             an error status nothing has been launched.  The descriptor, the
  *             scalars and the combination of arguments are checked first; a
  *             tensor with no blocks (rows or cols 0) then returns MASKGS_OK
- *             without reading or checking any array pointer.  Data-dependent
+ *             and launches nothing (the array pointers of its data are not
+ *             checked).  Data-dependent
  *             conditions (NaN logits, priors matching no candidate) are not
  *             errors; their behaviour is stated per entry point.
  */
