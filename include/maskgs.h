@@ -34,9 +34,9 @@
  *             scalars and the combination of arguments are checked first; a
  *             tensor with no blocks (rows or cols 0) then returns MASKGS_OK
  *             and launches nothing (the array pointers of its data are not
- *             checked).  Data-dependent
- *             conditions (NaN logits, priors matching no candidate) are not
- *             errors; their behaviour is stated per entry point.
+ *             checked).  Data-dependent conditions (NaN logits, priors
+ *             matching no candidate) are not errors; their behaviour is stated
+ *             per entry point.
  */
 #ifndef MASKGS_H
 #define MASKGS_H
