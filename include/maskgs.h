@@ -28,6 +28,9 @@
  *             bwd with accumulate reads and writes dz).
  *   Streams.  Work is enqueued on the given HIP stream (0 = null stream) and
  *             runs asynchronously; faults surface at the caller's synchronise.
+ *             Calls may be captured in a HIP graph: every argument, the
+ *             sample parameters included, is fixed at capture, and the arrays
+ *             are read when the graph runs.
  *   Errors.   Each call returns MASKGS_OK (0) or a MASKGS_E_* status.  All
  *             argument checks run on the host before anything is enqueued: on
  *             an error status nothing has been launched.  The descriptor, the
