@@ -533,6 +533,10 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    # the method's own bytes per block: what a forward (W, z in; W.M out) and a
+    # backward (W, z, G in; dz out) must move, plus the hard-mask outputs,
+    # whatever the kernels save in between (a saved soft index is not counted)
+    method_bpb = (M * wb + 4 * K + M * 2) + (M * wb + 4 * K + M * gb + 4 * K) + hard_out
     fwd_bwd_ms = ustats["fwd"]["ms_per_step"] + ustats["bwd"]["ms_per_step"]
     fb_bytes = per_block_bytes["fwd"] + per_block_bytes["bwd"]
     step_bytes = sum(per_block_bytes[k] for k in fused_kinds) * total_blocks
@@ -561,6 +565,11 @@ def main():
         # kernel of the step, every tensor) over the step time
         "step_hbm_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        # the same step counted on the method's own bytes (method_bytes_per_block)
+        "method_bytes_per_block": method_bpb,
+        "method_hbm_gbs": round(method_bpb * total_blocks / (ms_step * 1e-3) / 1e9, 1),
+        "method_hbm_frac": round(method_bpb * total_blocks / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                 4),
         "fwd_bwd_blocks_per_s": round(total_blocks / (fwd_bwd_ms * 1e-3), 1),  # unfused fwd + bwd
         "fwd_bwd_hbm_gbs": round(fb_bytes * total_blocks / (fwd_bwd_ms * 1e-3) / 1e9, 1),
         "kernels": kstats,
@@ -588,6 +597,32 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def host_cpu():
+    """The host the CPU baseline ran on: logical CPUs, the CPUs this process
+    may use, and the CPU model from /proc/cpuinfo."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "cpu_model": model}
+
+
+def oracle_threads():
+    """OpenMP threads for the oracle: OMP_NUM_THREADS if set, else every CPU
+    this process may use."""
+    env = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    return env or host_cpu()["usable_cpus"] or 1
+
+
 def cpu_baseline(wl, bufs, mg, min_secs=10.0):
     """The CPU oracle (all host threads) on whole layers of the workload, in
     order, until at least `min_secs` of CPU work: fwd + bwd + hard extract."""
@@ -595,8 +630,7 @@ def cpu_baseline(wl, bufs, mg, min_secs=10.0):
     import torch
     import oracle
 
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count() or 1
-    oracle.set_threads(threads)
+    oracle.set_threads(oracle_threads())
     used = oracle.get_threads()
     blocks = 0
     secs = 0.0
@@ -625,18 +659,21 @@ def cpu_baseline(wl, bufs, mg, min_secs=10.0):
             del wu, wf, zf, gf
         layers += 1
     return {"value": round(blocks / secs, 1), "unit": "weight-blocks/s", "cores": used,
-            "kind": "oracle",
+            "kind": "oracle", "host": host_cpu(),
             "sample": f"first {layers} layer(s) of the same workload ({tensors} tensors, "
                       f"{blocks} blocks): fwd + bwd + hard extract, {secs:.1f} s of CPU time"}
 
 
 def cpu_baseline_linear(wl, bufs, mp_bufs, min_secs=8.0):
-    """The CPU oracle of the linear-space variant (one thread) on whole tensors
-    of the workload, in order, until at least `min_secs` of CPU work: draw +
-    masked weights, then the policy gradient of the saved draw order."""
+    """The CPU oracle of the linear-space variant (all host threads) on whole
+    tensors of the workload, in order, until at least `min_secs` of CPU work:
+    draw + masked weights, then the policy gradient of the saved draw order."""
     import numpy as np
     import torch
     import oracle
+
+    oracle.set_threads(oracle_threads())
+    used = oracle.get_threads()
 
     blocks = 0
     secs = 0.0
@@ -660,8 +697,8 @@ def cpu_baseline_linear(wl, bufs, mp_bufs, min_secs=8.0):
         blocks += d["B"]
         tensors += 1
         del wf, pf, f
-    return {"value": round(blocks / secs, 1), "unit": "weight-blocks/s", "cores": 1,
-            "kind": "oracle",
+    return {"value": round(blocks / secs, 1), "unit": "weight-blocks/s", "cores": used,
+            "kind": "oracle", "host": host_cpu(),
             "sample": f"first {tensors} tensor(s) of the same workload ({blocks} blocks): draw + "
                       f"masked weights + policy gradient, {secs:.1f} s of CPU time"}
 

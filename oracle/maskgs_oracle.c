@@ -410,36 +410,59 @@ int orc_hard_extract(int n, int m, int64_t rows, int64_t cols, const float *z,
     orc_ctx c;
     if (orc_setup(&c, n, m, rows, cols, 0, 0, 0, 0, 1.0f, 1.0f, 0)) return -1;
     if ((values || val_idx) && !(n == 2 && m == 4)) return -2;
-    int64_t nbits = c.nblocks * c.m;
-    if (bits) memset(bits, 0, (size_t)((nbits + 7) / 8));
-    if (val_idx) memset(val_idx, 0, (size_t)((c.nblocks + 1) / 2));
+    if (c.nblocks == 0) return 0;
+    /* pass 1, one block at a time (blocks are independent): the argmax, and
+     * the kept values of 2:4 blocks */
+    uint8_t *best_of = idx ? idx : (uint8_t *)malloc((size_t)c.nblocks);
+    if (!best_of) return -3;
+#pragma omp parallel for schedule(static)
     for (int64_t b = 0; b < c.nblocks; ++b) {
         const float *zb = z + b * c.k;
         int best = 0;
         for (int i = 1; i < c.k; ++i)
             if (zb[i] > zb[best]) best = i;
-        if (idx) idx[b] = (uint8_t)best;
-        uint8_t mask = c.cand[best];
-        if (bits)
-            for (int j = 0; j < c.m; ++j)
-                if (mask & (1u << j)) {
-                    int64_t bit = b * c.m + j;
-                    bits[bit >> 3] |= (uint8_t)(1u << (bit & 7));
-                }
-        if (values || val_idx) {
+        best_of[b] = (uint8_t)best;
+        if (values) {
+            uint8_t mask = c.cand[best];
             int pos[2], t = 0;
             for (int j = 0; j < 4; ++j)
                 if (mask & (1u << j)) pos[t++] = j;
-            if (values)
-                for (int u = 0; u < 2; ++u)
-                    memcpy((char *)values + (b * 2 + u) * w_bytes,
-                           (const char *)w_raw + (b * 4 + pos[u]) * w_bytes, (size_t)w_bytes);
-            if (val_idx) {
-                uint8_t nib = (uint8_t)(pos[0] | (pos[1] << 2));
-                val_idx[b >> 1] |= (uint8_t)((b & 1) ? (nib << 4) : nib);
-            }
+            for (int u = 0; u < 2; ++u)
+                memcpy((char *)values + (b * 2 + u) * w_bytes,
+                       (const char *)w_raw + (b * 4 + pos[u]) * w_bytes, (size_t)w_bytes);
         }
     }
+    /* pass 2, one output byte at a time (a byte holds the bits or nibbles of
+     * several blocks): the packed masks S_k and the 2:4 index nibbles */
+    if (bits) {
+        const int64_t nbytes = (c.nblocks * c.m + 7) / 8;
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < nbytes; ++i) {
+            uint8_t v = 0;
+            for (int64_t bit = 8 * i; bit < 8 * i + 8 && bit < c.nblocks * c.m; ++bit) {
+                const int64_t b = bit / c.m;
+                if (c.cand[best_of[b]] & (1u << (bit % c.m))) v |= (uint8_t)(1u << (bit - 8 * i));
+            }
+            bits[i] = v;
+        }
+    }
+    if (val_idx) {
+        const int64_t nbytes = (c.nblocks + 1) / 2;
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < nbytes; ++i) {
+            uint8_t v = 0;
+            for (int64_t b = 2 * i; b < 2 * i + 2 && b < c.nblocks; ++b) {
+                uint8_t mask = c.cand[best_of[b]];
+                int pos[2], t = 0;
+                for (int j = 0; j < 4; ++j)
+                    if (mask & (1u << j)) pos[t++] = j;
+                uint8_t nib = (uint8_t)(pos[0] | (pos[1] << 2));
+                v |= (uint8_t)((b & 1) ? (nib << 4) : nib);
+            }
+            val_idx[i] = v;
+        }
+    }
+    if (!idx) free(best_of);
     return 0;
 }
 

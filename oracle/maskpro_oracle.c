@@ -85,26 +85,44 @@ int orc_mp_fwd(int n, int m, int64_t rows, int64_t cols, uint64_t block_offset,
                uint16_t *out_bf16, float *out_f32) {
     int64_t nb;
     if (orc_mp_shape(n, m, rows, cols, &nb)) return -1;
-    if (bits) memset(bits, 0, (size_t)((nb * m + 7) / 8));
+    if (nb == 0) return 0;
+    /* pass 1, one block at a time (blocks are independent): the draw, its
+     * order and the masked weights; the kept set of each block is kept for
+     * pass 2 */
+    uint8_t *keep_of = (uint8_t *)malloc((size_t)nb);
+    if (!keep_of) return -3;
+#pragma omp parallel for schedule(static)
     for (int64_t b = 0; b < nb; ++b) {
         int order[8];
         orc_mp_draw(n, m, seed, step, tensor_id, block_offset + (uint64_t)b, flags, pi + b * m,
                     order);
         int keep[8] = {0};
+        uint8_t kmask = 0;
         for (int k = 0; k < n; ++k) {
             keep[order[k]] = 1;
+            kmask |= (uint8_t)(1u << order[k]);
             if (order_out) order_out[b * n + k] = (uint8_t)order[k];
         }
+        keep_of[b] = kmask;
         for (int j = 0; j < m; ++j) {
             double u = keep[j] ? (double)w[b * m + j] : 0.0;
             if (out_bf16) out_bf16[b * m + j] = orc_bf16_from_double(u);
             if (out_f32) out_f32[b * m + j] = (float)u;
-            if (bits && keep[j]) {
-                int64_t bit = b * m + j;
-                bits[bit >> 3] |= (uint8_t)(1u << (bit & 7));
-            }
         }
     }
+    /* pass 2, one byte of the LSB-first mask stream at a time (a byte holds
+     * the bits of several blocks when m < 8) */
+    if (bits) {
+        const int64_t nbits = nb * m, nbytes = (nbits + 7) / 8;
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < nbytes; ++i) {
+            uint8_t v = 0;
+            for (int64_t bit = 8 * i; bit < 8 * i + 8 && bit < nbits; ++bit)
+                if (keep_of[bit / m] & (1u << (bit % m))) v |= (uint8_t)(1u << (bit - 8 * i));
+            bits[i] = v;
+        }
+    }
+    free(keep_of);
     return 0;
 }
 
@@ -145,6 +163,8 @@ int orc_mp_grad(int n, int m, int64_t rows, int64_t cols, uint64_t block_offset,
                 const float *dpi_prev, double *dpi) {
     int64_t nb;
     if (orc_mp_shape(n, m, rows, cols, &nb)) return -1;
+    /* blocks are independent: each writes only its own M gradients */
+#pragma omp parallel for schedule(static)
     for (int64_t b = 0; b < nb; ++b) {
         const float *p = pi + b * m;
         int order[8];

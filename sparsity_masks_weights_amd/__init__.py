@@ -417,11 +417,18 @@ _MaskedWeight = None
 
 def masked_weight(z, w, t: Tensor, p: SampleParams, lam: float = 0.0, save_y: bool = True,
                   out_dtype=None):
-    """(W (.) M~, R) with autograd to z; see _masked_weight_function."""
+    """(W (.) M~, R) with autograd to z; see _masked_weight_function.
+
+    save_y keeps the soft index for the backward; under MASKGS_HARD_SAMPLE the
+    backward must recompute it from z (it needs the sample's argmax, which a
+    saved fp32 soft index does not determine), so the soft index is then never
+    saved, whatever save_y says."""
     global _MaskedWeight
     torch = _torch()
     if _MaskedWeight is None:
         _MaskedWeight = _masked_weight_function()
+    if p.flags & MASKGS_HARD_SAMPLE:
+        save_y = False
     return _MaskedWeight.apply(z, w, t, p, lam, save_y,
                                torch.bfloat16 if out_dtype is None else out_dtype)
 

@@ -47,7 +47,11 @@ int check_desc(const maskgs_tensor_desc *t, Geometry *g) {
     if (!((t->n == 2 && t->m == 4) || (t->n == 4 && t->m == 8))) return MASKGS_E_UNSUPPORTED;
     if (t->rows < 0 || t->cols < 0 || t->cols % t->m != 0) return MASKGS_E_SHAPE;
     const int64_t bpr = t->cols / t->m;
-    if (bpr != 0 && t->rows > (INT64_C(1) << 56) / (bpr * 80)) return MASKGS_E_SHAPE;
+    // rows * bpr * 80 <= 2^56, tested without forming a product that could
+    // overflow: bpr is bounded first, so bpr * 80 <= 2^56 below
+    constexpr int64_t kLimit = INT64_C(1) << 56;
+    if (bpr > kLimit / 80) return MASKGS_E_SHAPE;
+    if (bpr != 0 && t->rows > kLimit / (bpr * 80)) return MASKGS_E_SHAPE;
     g->n = t->n;
     g->m = t->m;
     g->k = (t->m == 4) ? 6 : 70;

@@ -55,3 +55,36 @@ def assert_out(got, ref, what):
         assert_bf16_ulp(got, ref, what)
     else:
         assert_close(got, ref, what)
+
+
+def sample_rows(rows):
+    """Every 61st row plus the first and the last."""
+    return sorted(set(range(0, rows, 61)) | {rows - 1})
+
+
+def check_rows(orc, n, m, spec, p, w, z, G, lam, y, out, dz, what):
+    """The oracle on sampled rows of one tensor against the GPU's whole-tensor
+    outputs: the soft index y (skipped when None: not saved), the masked
+    weight and the logit gradient.  A row range is a tensor with a block
+    offset, so the oracle draws the noise of the whole tensor."""
+    import torch
+    bpr = spec.cols // m
+    rows = sample_rows(spec.rows)
+    K = z.shape[1]
+    sel = torch.tensor(rows, device=w.device)
+    bsel = (sel[:, None] * bpr + torch.arange(bpr, device=w.device)[None, :]).reshape(-1)
+    wn = to_np(w.index_select(0, sel))
+    zn = to_np(z.index_select(0, bsel)).reshape(len(rows), bpr, K)
+    Gn = to_np(G.index_select(0, sel))
+    yg = None if y is None else to_np(y.index_select(0, bsel)).reshape(len(rows), bpr, K)
+    og = to_np(out.index_select(0, sel))
+    dg = to_np(dz.index_select(0, bsel)).reshape(len(rows), bpr, K)
+    for i, r in enumerate(rows):
+        kw = dict(kappa=p.kappa, tau=p.tau, seed=p.seed, step=p.step,
+                  tensor_id=spec.tensor_id, block_offset=r * bpr)
+        f = orc.fwd(n, m, widen(wn[i:i + 1]), zn[i], **kw)
+        if yg is not None:
+            assert_close(yg[i], f["y"], f"{what} row {r} y")
+        assert_out(og[i:i + 1], f["out"], f"{what} row {r} out")
+        d = orc.bwd(n, m, widen(wn[i:i + 1]), zn[i], widen(Gn[i:i + 1]), lam=lam, **kw)
+        assert_close(dg[i], d, f"{what} row {r} dz")

@@ -108,6 +108,16 @@ int main() {
            MASKGS_E_SHAPE);
     EXPECT(maskgs_fwd(&huge, &p, A, MASKGS_BF16, Af, A, MASKGS_BF16, Af, Ad, nullptr),
            MASKGS_E_SHAPE);
+    // (cols/m) * 80 past int64: 2^62 columns wrap the product to 0, and
+    // 3689348814741910324 columns wrap it to 16; both are shape errors
+    for (const int64_t wide_cols : {INT64_C(1) << 62, INT64_C(3689348814741910324)})
+        for (const int64_t r : {INT64_C(0), INT64_C(1)}) {
+            const maskgs_tensor_desc wide{2, 4, r, wide_cols, 0, 0};
+            EXPECT(maskgs_fwd(&wide, &p, A, MASKGS_BF16, Af, A, MASKGS_BF16, Af, Ad, nullptr),
+                   MASKGS_E_SHAPE);
+            EXPECT(maskpro_fwd(&wide, &dp, A, MASKGS_BF16, Af, A, MASKGS_BF16, Ab, Ab, nullptr),
+                   MASKGS_E_SHAPE);
+        }
     EXPECT(maskgs_fwd(&empty, &p, nullptr, MASKGS_BF16, nullptr, nullptr, MASKGS_BF16, nullptr,
                       nullptr, nullptr),
            MASKGS_OK);

@@ -66,6 +66,16 @@ def test_fwd_validation(L):
         top = (1 << 56) // (bpr * 80)
         n_ = 2 if m_ == 4 else 4
         assert _fwd(L, desc=mg.TensorDesc(n_, m_, top + 1, cols, 0, 0)) == mg.MASKGS_E_SHAPE
+    # columns so wide that (cols/m) * 80 leaves int64: 2^62 columns (the product
+    # wraps to 0) and 3689348814741910324 columns (it wraps to 16) are refused,
+    # also with an empty or a single row, instead of dividing by zero or
+    # accepting ~9.2e17 blocks
+    for cols in (1 << 62, 3689348814741910324):
+        for rows in (0, 1):
+            assert _fwd(L, desc=mg.TensorDesc(2, 4, rows, cols, 0, 0)) == mg.MASKGS_E_SHAPE
+    wide = (1 << 56) // 80 * 4  # the widest tensor of one row, and one block more
+    assert _fwd(L, desc=mg.TensorDesc(2, 4, 0, wide, 0, 0)) == mg.MASKGS_OK
+    assert _fwd(L, desc=mg.TensorDesc(2, 4, 0, wide + 4, 0, 0)) == mg.MASKGS_E_SHAPE
     assert _fwd(L, desc=mg.TensorDesc(2, 4, 0, 16, 1 << 56, 0)) == mg.MASKGS_OK
     assert _fwd(L, desc=mg.TensorDesc(2, 4, 0, 16, (1 << 56) + 1, 0)) == mg.MASKGS_E_SHAPE
     assert _fwd(L, desc=mg.TensorDesc(4, 8, 0, 16, 2**64 - 1, 0)) == mg.MASKGS_E_SHAPE

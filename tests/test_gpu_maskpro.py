@@ -7,11 +7,11 @@ Bars:
     fp32(pi + g) decide the draw on both sides in the same precision; the
     masked weight is a copy of the kept weight);
   - the initial logits: bit-exact;
-  - the policy gradient dpi = A * dlogp: |d| <= N * 1e-6 * |A| + 1e-5 |ref|.
+  - the policy gradient dpi = A * dlogp: |d| <= 1e-6 * max(1, |A|) + 1e-5 |ref|.
     Each of the N rounds adds or subtracts a term e/Z in [0, 1] that the fp32
     kernel forms with a few roundings (exp, the sum Z of at most M terms, the
-    reciprocal, the product), about 10 ulp = 6e-7 of the term's unit scale, so
-    the absolute error of dlogp stays below N * 1e-6; A scales it.
+    reciprocal, the product); the error of dlogp measured at most 4.6e-7 of
+    its unit scale, within the 1e-6 absolute bound, and A scales it.
 Small shapes in full (several 256-block workgroups and a ragged tail, odd and
 even global block offsets), the draw's Plackett-Luce frequencies, then one
 full-size tensor per pattern on sampled rows.
@@ -65,7 +65,9 @@ def _order_tensor(B, m, dev):
 
 
 def assert_pg(got, ref, adv, n, what):
-    assert_close(got, ref, what, rtol=1e-5, atol=n * 1e-6 * abs(adv))
+    # dlogp is a unit-scale quantity and A multiplies it, so the absolute bound
+    # 1e-6 holds for |A| <= 1 and scales with |A| beyond
+    assert_close(got, ref, what, rtol=1e-5, atol=1e-6 * max(1.0, abs(adv)))
 
 
 CASES = [

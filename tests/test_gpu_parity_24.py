@@ -307,11 +307,14 @@ def test_fwd_hard_equals_fwd_then_extract(dev, mg, orc, case):
     assert np.array_equal(to_np(bits), h["bits"]) and np.array_equal(to_np(vals), h["values"])
 
 
-@pytest.mark.parametrize("save_y", [True, False])
-def test_autograd_pairing_matches_the_abi_calls(mg, save_y):
+@pytest.mark.parametrize("save_y,flags", [(True, 0), (False, 0), (True, 2), (False, 2)])
+def test_autograd_pairing_matches_the_abi_calls(mg, save_y, flags):
     """masked_weight (torch.autograd.Function over maskgs_fwd / maskgs_bwd)
-    gives exactly the outputs of the direct calls."""
+    gives exactly the outputs of the direct calls, also under the hard sample
+    (flags 2), where the backward recomputes the soft index whatever save_y
+    asks."""
     import torch
+    assert flags in (0, mg.MASKGS_HARD_SAMPLE)
     rows, cols = 37, 72
     B = rows * cols // 4
     dev = torch.device("cuda:0")
@@ -319,7 +322,7 @@ def test_autograd_pairing_matches_the_abi_calls(mg, save_y):
     z0 = _rand((B, 6), 1.0, torch.float32, dev, 91)
     G = _rand((rows, cols), 1e-3, torch.bfloat16, dev, 92)
     t = mg.Tensor(2, 4, rows, cols, 5, 3)
-    p = mg.sample_params(11, 2, 100.0, 4.0)
+    p = mg.sample_params(11, 2, 100.0, 4.0, flags)
     z = z0.clone().requires_grad_(True)
     out, reg = mg.masked_weight(z, w, t, p, lam=1e-5, save_y=save_y)
     out.backward(G)

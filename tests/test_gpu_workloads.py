@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 from conftest import gpu_available
-from gpu_helpers import assert_bf16_ulp, assert_close, to_np, widen
+from gpu_helpers import assert_close, check_rows, to_np, widen
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
@@ -21,35 +21,6 @@ def mg():
     import sparsity_masks_weights_amd as mg
     mg.load_library()
     return mg
-
-
-def sample_rows(rows):
-    return sorted(set(range(0, rows, 61)) | {rows - 1})
-
-
-def check_rows(orc, n, m, spec, p, w, z, G, lam, y, out, dz, what, prior=None):
-    """Oracle on sampled rows vs the GPU's whole-tensor outputs."""
-    bpr = spec.cols // m
-    rows = sample_rows(spec.rows)
-    K = z.shape[1]
-    ridx = np.array(rows)
-    import torch
-    sel = torch.from_numpy(ridx).to(w.device)
-    bsel = (sel[:, None] * bpr + torch.arange(bpr, device=w.device)[None, :]).reshape(-1)
-    wn = to_np(w.index_select(0, sel))
-    zn = to_np(z.index_select(0, bsel)).reshape(len(rows), bpr, K)
-    Gn = to_np(G.index_select(0, sel))
-    yg = to_np(y.index_select(0, bsel)).reshape(len(rows), bpr, K)
-    og = to_np(out.index_select(0, sel))
-    dg = to_np(dz.index_select(0, bsel)).reshape(len(rows), bpr, K)
-    for i, r in enumerate(rows):
-        kw = dict(kappa=p.kappa, tau=p.tau, seed=p.seed, step=p.step,
-                  tensor_id=spec.tensor_id, block_offset=r * bpr)
-        f = orc.fwd(n, m, widen(wn[i:i + 1]), zn[i], **kw)
-        assert_close(yg[i], f["y"], f"{what} row {r} y")
-        assert_bf16_ulp(og[i:i + 1], f["out"], f"{what} row {r} out")
-        d = orc.bwd(n, m, widen(wn[i:i + 1]), zn[i], widen(Gn[i:i + 1]), lam=lam, **kw)
-        assert_close(dg[i], d, f"{what} row {r} dz")
 
 
 def run_tensor(mg, wl, spec, dev, p, w, z, G):

@@ -547,6 +547,39 @@ def test_thread_count_invariance(orc):
     assert math.isclose(a["reg"], b["reg"], rel_tol=1e-12)
 
 
+@pytest.mark.parametrize("n,m,rows,cols", [(2, 4, 37, 72), (4, 8, 13, 56), (2, 4, 1, 4)])
+def test_thread_count_invariance_of_the_packing_passes(orc, n, m, rows, cols):
+    """The hard extraction and the linear-space draw and gradient split their
+    work over threads by block, then pack bits and nibbles by output byte; the
+    results must not depend on the thread count (odd block counts, so threads
+    meet inside a shared byte)."""
+    rng = np.random.default_rng(61)
+    B = rows * cols // m
+    K = len(orc.candidates(n, m))
+    z = rng.standard_normal((B, K)).astype(np.float32)
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    pi = rng.standard_normal((B, m)).astype(np.float32)
+    old = orc.get_threads()
+    res = []
+    try:
+        for t in (1, 3, 4):
+            orc.set_threads(t)
+            h = orc.hard_extract(n, m, z, rows, cols, w_raw=w if (n, m) == (2, 4) else None)
+            f = orc.maskpro_fwd(n, m, w, pi, seed=5, step=1, tensor_id=2, block_offset=3)
+            g = orc.maskpro_grad(n, m, pi, rows, cols, advantage=0.7, seed=5, step=1,
+                                 tensor_id=2, block_offset=3)
+            res.append((h, f, g))
+    finally:
+        orc.set_threads(old)
+    for h, f, g in res[1:]:
+        for k in ("idx", "bits", "values", "val_idx"):
+            a, b = res[0][0][k], h[k]
+            assert (a is None and b is None) or np.array_equal(a, b), k
+        for k in ("order", "bits", "out"):
+            assert np.array_equal(res[0][1][k], f[k]), k
+        assert np.array_equal(res[0][2], g)
+
+
 def test_steps_and_tensors_draw_fresh_noise(orc):
     """Section 3.4, Algorithm 1: independent noise per step; the counter also
     separates tensors, so layers do not share draws."""
