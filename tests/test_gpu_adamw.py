@@ -129,7 +129,7 @@ def test_bwd_adamw_mlp_tensor_sampled_rows(mg, orc):
     fused update from a saved soft index at t = 3, oracle on sampled rows."""
     import torch
     from workloads import WORKLOADS, tensor_inputs
-    from test_gpu_workloads import sample_rows
+    from gpu_helpers import sample_rows
     wl = WORKLOADS["llama7b_all_linear"]
     spec = [s for s in wl.tensors if s.rows == 11008][0]
     dev = torch.device("cuda:0")

@@ -252,7 +252,7 @@ def test_full_size_tensor_sampled_rows(mg, orc, wl_key, name):
     whole tensor on the GPU, the oracle on every 61st row and the last."""
     import torch
     from workloads import WORKLOADS, linear_logits, tensor_inputs
-    from test_gpu_workloads import sample_rows
+    from gpu_helpers import sample_rows
     wl = WORKLOADS[wl_key]
     spec = [s for s in wl.tensors if s.name == name][0]
     n, m = wl.n, wl.m
