@@ -12,7 +12,8 @@ import pytest
 
 from conftest import gpu_available
 from gpu_helpers import assert_bf16_ulp, assert_close, assert_out, to_np, widen
-from test_gpu_workloads import check_rows, run_tensor
+from gpu_helpers import check_rows
+from test_gpu_workloads import run_tensor
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
