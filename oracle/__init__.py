@@ -69,8 +69,8 @@ def lib():
     L.orc_philox_words.argtypes = [c.c_uint64, c.c_uint32, c.c_uint32, c.c_uint64, c.c_int64, P]
     L.orc_uniform.argtypes = [c.c_uint32]
     L.orc_uniform.restype = c.c_float
-    L.orc_ln_contract.argtypes = [c.c_float]
-    L.orc_ln_contract.restype = c.c_float
+    L.orc_gumbel_coef.argtypes = [P]
+    L.orc_gumbel_coef.restype = None
     L.orc_gumbel.argtypes = [c.c_uint32]
     L.orc_gumbel.restype = c.c_float
     L.orc_gumbel_all.argtypes = [P]
@@ -166,8 +166,12 @@ def uniform(x: int) -> float:
     return float(lib().orc_uniform(int(x)))
 
 
-def ln_contract(x: float) -> float:
-    return float(lib().orc_ln_contract(float(x)))
+def gumbel_coef() -> np.ndarray:
+    """The noise contract's fp32 Taylor coefficients, [side, binade, segment, 4]
+    = (2, 24, 32, 4), c0..c3 of -ln(-ln eps) about each segment centre."""
+    out = np.zeros((2, 24, 32, 4), dtype=np.float32)
+    lib().orc_gumbel_coef(_ptr(out))
+    return out
 
 
 def gumbel(x: int) -> float:

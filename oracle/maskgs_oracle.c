@@ -150,62 +150,102 @@ void orc_philox_words(uint64_t seed, uint32_t step, uint32_t tensor_id, uint64_t
 /* Uniform: eps = (2*(x >> 9) + 1) * 2^-24, exact in fp32, strictly inside   */
 /* (0, 1) as the Gumbel inverse CDF needs.                                    */
 /* Gumbel (MaskLLM summary, section 3.4, Eq. 5): g = -ln(-ln eps), natural   */
-/* logarithm, evaluated in fp32 with the contract logarithm ln_c below.      */
+/* logarithms, for each of the 2^23 values eps can take.  The pages fix no   */
+/* precision; the value each side uses is defined in fp32 as the cubic        */
+/* Taylor polynomial of -ln(-ln eps) about the centre of the segment that    */
+/* holds eps, evaluated with three fused multiply-adds:                       */
+/*   - k2 = 2*(x >> 9) + 1 (the odd integer eps * 2^24); side 0 when          */
+/*     eps < 1/2 (v = k2), side 1 when eps > 1/2 (v = 2^24 - k2, i.e. the     */
+/*     same integer for 1 - eps);                                             */
+/*   - v lies in [2^b, 2^(b+1)); its binade splits into 32 segments of width  */
+/*     2^(b-5), segment q = the five bits after the leading one of v;         */
+/*   - d = v / 2^b - 1 - (q + 1/2)/32, the offset from the segment centre,     */
+/*     exact in fp32, |d| <= 1/64;                                            */
+/*   - g = ((c3*d + c2)*d + c1)*d + c0 with the Taylor coefficients c_n of    */
+/*     -ln(-ln eps) in d about the centre, each evaluated in fp64 and rounded */
+/*     once to fp32 (orc_gumbel_coef).                                        */
+/* Over all 2^23 uniforms this stays within 1.25 ulp of max(|g|, 1) of the   */
+/* exact value (pinned exhaustively by the tests).                            */
 /* ------------------------------------------------------------------------- */
 float orc_uniform(uint32_t x) {
     uint32_t k = x >> 9;
     return (float)(2u * k + 1u) * 0x1p-24f;
 }
 
-/* ln_c: the fp32 natural logarithm of the Cephes Math Library (S. L. Moshier,
- * single-precision logf): x = 2^e * mm with mm in [0.5, 1); mm below sqrt(1/2)
- * is doubled (e decremented), so f = mm - 1 lies in [sqrt(1/2)-1, sqrt(2)-1);
- * ln(1+f) = f - f^2/2 + f^3 * P(f) with Cephes' degree-8 P, and e*ln(2) is
- * added in two parts (0.693359375 exact, -2.12194440e-4 the remainder).
- * Fixed operation order, every a*b+c written as one fmaf; x must be a
- * positive normal number (all arguments the noise uses are). */
-float orc_ln_contract(float x) {
-    uint32_t bits;
-    memcpy(&bits, &x, 4);
-    int e = (int)(bits >> 23) - 126;
-    uint32_t mb = (bits & 0x007FFFFFu) | 0x3F000000u;
-    float mm;
-    memcpy(&mm, &mb, 4);
-    float f;
-    if (mm < 0.707106781186547524f) {
-        e -= 1;
-        f = (mm + mm) - 1.0f;
+#define ORC_GS_BINADES 24
+#define ORC_GS_SEGS 32
+
+static float orc_gs[2][ORC_GS_BINADES][ORC_GS_SEGS][4];
+
+/* Taylor coefficients c0..c3 of segment (side, b, q), as the step in d moves
+ * eps by 2^(b-24) (side 0) or 1 - eps by 2^(b-24) (side 1).  With delta the
+ * centre's eps (side 0) or 1 - eps (side 1):
+ *   side 0: L = -ln(delta), g = -ln L, dg/d(delta) = 1/(delta L), and the
+ *           n-th derivative in d is (2^(b-24)/delta)^n times
+ *           1/L, (1/L^2 - 1/L), (2/L^3 - 3/L^2 + 2/L)          for n = 1, 2, 3;
+ *   side 1: M = -ln(1 - delta), g = -ln M, and in d the derivatives are
+ *           (2^(b-24)/(1 - delta))^n times
+ *           -1/M, (1/M^2 - 1/M), (-2/M^3 + 3/M^2 - 2/M);
+ * c_n = derivative / n!. */
+static void orc_gumbel_coef_fill(int side, int b, int q, double co[4]) {
+    double vc = ldexp(1.0 + (q + 0.5) / 32.0, b);
+    double delta = vc * 0x1p-24;
+    if (side == 0) {
+        double L = -log(delta);
+        double rho = ldexp(1.0, b) / vc;
+        double iL = 1.0 / L;
+        co[0] = -log(L);
+        co[1] = rho * iL;
+        co[2] = rho * rho * (iL * iL - iL) / 2.0;
+        co[3] = rho * rho * rho * (2.0 * iL * iL * iL - 3.0 * iL * iL + 2.0 * iL) / 6.0;
     } else {
-        f = mm - 1.0f;
+        double M = -log1p(-delta);
+        double sig = ldexp(1.0, b - 24) / (1.0 - delta);
+        double iM = 1.0 / M;
+        co[0] = -log(M);
+        co[1] = -sig * iM;
+        co[2] = sig * sig * (iM * iM - iM) / 2.0;
+        co[3] = sig * sig * sig * (-2.0 * iM * iM * iM + 3.0 * iM * iM - 2.0 * iM) / 6.0;
     }
-    float z = f * f;
-    float p = 7.0376836292e-2f;
-    p = fmaf(p, f, -1.1514610310e-1f);
-    p = fmaf(p, f, 1.1676998740e-1f);
-    p = fmaf(p, f, -1.2420140846e-1f);
-    p = fmaf(p, f, 1.4249322787e-1f);
-    p = fmaf(p, f, -1.6668057665e-1f);
-    p = fmaf(p, f, 2.0000714765e-1f);
-    p = fmaf(p, f, -2.4999993993e-1f);
-    p = fmaf(p, f, 3.3333331174e-1f);
-    float y = (p * f) * z;
-    float fe = (float)e;
-    y = fmaf(fe, -2.12194440e-4f, y);
-    y = fmaf(-0.5f, z, y);
-    float r = f + y;
-    r = fmaf(fe, 0.693359375f, r);
-    return r;
 }
 
+__attribute__((constructor)) static void orc_gumbel_coef_init(void) {
+    for (int side = 0; side < 2; ++side)
+        for (int b = 0; b < ORC_GS_BINADES; ++b)
+            for (int q = 0; q < ORC_GS_SEGS; ++q) {
+                double co[4];
+                orc_gumbel_coef_fill(side, b, q, co);
+                for (int n = 0; n < 4; ++n) orc_gs[side][b][q][n] = (float)co[n];
+            }
+}
+
+/* The fp32 coefficient table, [side][binade][segment][c0..c3] (1536 x 4). */
+void orc_gumbel_coef(float *out) { memcpy(out, orc_gs, sizeof(orc_gs)); }
+
 float orc_gumbel(uint32_t x) {
-    float eps = orc_uniform(x);
-    float t = -orc_ln_contract(eps);
-    return -orc_ln_contract(t);
+    uint32_t k2 = 2u * (x >> 9) + 1u;
+    int side = k2 > (1u << 23);
+    uint32_t v = side ? (1u << 24) - k2 : k2;
+    int b = 0;
+    while ((v >> (b + 1)) != 0) ++b;                   /* v in [2^b, 2^(b+1)) */
+    uint32_t frac = v - (1u << b);                     /* v/2^b = 1 + frac/2^b */
+    uint32_t q, r;                                     /* frac/2^b = q/32 + r/2^b */
+    if (b >= 5) {
+        q = frac >> (b - 5);
+        r = frac - (q << (b - 5));
+    } else {
+        q = frac << (5 - b);
+        r = 0;
+    }
+    float d = (float)r * ldexpf(1.0f, -b) - 0x1p-6f;   /* exact */
+    const float *c = orc_gs[side][b][q];
+    return fmaf(fmaf(fmaf(c[3], d, c[2]), d, c[1]), d, c[0]);
 }
 
 /* g for every one of the 2^23 distinct uniforms, indexed by x >> 9. */
 void orc_gumbel_all(float *out) {
-    for (uint32_t k = 0; k < (1u << 23); ++k) out[k] = orc_gumbel(k << 9);
+#pragma omp parallel for schedule(static)
+    for (int32_t k = 0; k < (1 << 23); ++k) out[k] = orc_gumbel((uint32_t)k << 9);
 }
 
 /* ------------------------------------------------------------------------- */
