@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-train-step", action="store_true",
                     help="skip the training step with the fused AdamW update")
+    ap.add_argument("--step", choices=("recompute", "saved"), default="recompute",
+                    help="recompute: the backward draws the soft index again from z; "
+                         "saved: the forward writes it and the backward reads it")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -147,7 +150,7 @@ def main():
         return None if t is None else P(t.data_ptr())
 
     # pre-marshalled argument tuples: the timed loop only calls the C ABI
-    calls = {"fwd": [], "bwd": [], "hard": []}
+    calls = {"fwd": [], "bwd": [], "hard": [], "fwd_hard_noy": [], "bwd_rc": []}
     fused = []
     params = [mg.SampleParams(0, 0, wl.kappa, wl.tau, 0)]
     pref = ctypes.byref(params[0])
@@ -164,6 +167,13 @@ def main():
         fused.append((L.maskgs_fwd_hard, (dref, pref, ptr(d["w"]), bf, ptr(d["z"]), ptr(d["out"]),
                                           bf, ptr(d["y"]), ptr(reg), None, ptr(d["bits"]),
                                           ptr(d["vals"]), ptr(d["vidx"]), sp(i))))
+        calls["fwd_hard_noy"].append((L.maskgs_fwd_hard, (dref, pref, ptr(d["w"]), bf, ptr(d["z"]),
+                                                          ptr(d["out"]), bf, None, ptr(reg), None,
+                                                          ptr(d["bits"]), ptr(d["vals"]),
+                                                          ptr(d["vidx"]), sp(i))))
+        calls["bwd_rc"].append((L.maskgs_bwd, (dref, pref, ptr(d["w"]), bf, ptr(d["z"]), None,
+                                               ptr(d["G"]), gdt, ctypes.c_float(wl.lam),
+                                               ptr(d["dz"]), 0, sp(i))))
 
     # per-block algorithmic bytes of each kernel (bf16 weights, fp32 logits)
     K, M, N = wl.k, wl.m, wl.n
@@ -174,6 +184,10 @@ def main():
         "fwd_hard": M * wb + 4 * K + M * 2 + 4 * K + hard_out,
         "bwd": M * wb + M * 2 + 4 * K + 4 * K,            # W, G, y in; dz out
         "hard": 4 * K + (M * wb if compact else 0) + hard_out,
+        # the soft index not saved: fwd (W, z in; W.M, hard outputs out) and the
+        # backward drawing it again (W, G, z in; dz out)
+        "fwd_hard_noy": M * wb + 4 * K + M * 2 + hard_out,
+        "bwd_rc": M * wb + M * 2 + 4 * K + 4 * K,
     }
     calls["fwd_hard"] = fused
     big = [i for i, d in enumerate(bufs) if d["B"] == max(x["B"] for x in bufs)]
@@ -186,7 +200,7 @@ def main():
     # logits fused in (one read of z and W), then the backward of every tensor.
     # Outputs are bit-identical to forward, backward, then extraction (z is not
     # written by the step); that unfused order is timed after the timed steps.
-    fused_kinds = ("fwd_hard", "bwd")
+    fused_kinds = ("fwd_hard_noy", "bwd_rc") if args.step == "recompute" else ("fwd_hard", "bwd")
     unfused_kinds = ("fwd", "bwd", "hard")
     phase = {k: [] for k in calls}
     launch_ev = {k: [] for k in calls}
@@ -240,7 +254,7 @@ def main():
     # the dominant kernel (largest share of a step) is chosen from the warmup
     # phases; its launches on the largest tensors are timed in the timed steps
     warm = {k: sum(a.elapsed_time(b) for a, b in v) for k, v in phase.items() if v}
-    dom = max(warm, key=warm.get) if args.warmup else "fwd_hard"
+    dom = max(warm, key=warm.get) if args.warmup else fused_kinds[0]
     for v in phase.values():
         v.clear()
     t0 = torch.cuda.Event(enable_timing=True)
@@ -558,8 +572,11 @@ def main():
                    "n_m": f"{wl.n}:{wl.m}", "weights": f"{wl.w_dtype} N(0,{wl.w_std})",
                    "logits": f"fp32 N(0,{wl.z_std})", "upstream_grad": f"{wl.g_dtype} N(0,{wl.g_std})",
                    "kappa": wl.kappa, "tau": wl.tau, "lambda": wl.lam,
-                   "step": "fwd (y saved, reg) with the hard mask of the same logits fused in "
-                           "(argmax, bit-pack, 2:4 compaction) + bwd (saved y)",
+                   "step": ("fwd (reg) with the hard mask of the same logits fused in (argmax, "
+                            "bit-pack, 2:4 compaction) + bwd drawing the soft index again from z"
+                            if args.step == "recompute" else
+                            "fwd (y saved, reg) with the hard mask of the same logits fused in "
+                            "(argmax, bit-pack, 2:4 compaction) + bwd (saved y)"),
                    "streams": args.streams, "parallelism": "single GPU"},
         # the whole timed step as one memory stream: its algorithmic bytes (every
         # kernel of the step, every tensor) over the step time

@@ -29,10 +29,13 @@ __global__ __launch_bounds__(kThreads) void philox_words_kernel(uint32_t k0, uin
 
 __global__ __launch_bounds__(kThreads) void gumbel_kernel(const uint32_t *words, int64_t n,
                                                           float *g) {
+    __shared__ float4 gtab[kGumbelRows];
+    load_gumbel_table<kThreads>(gtab);
+    __syncthreads();
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
     for (int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; t < n;
          t += stride)
-        g[t] = gumbel(words[t]);
+        g[t] = gumbel_lds(words[t], gtab);
 }
 
 }  // namespace

@@ -1,7 +1,7 @@
 // maskgs_device.hpp -- device building blocks of libmaskgs (gfx950): candidate
 // tables, the Philox4x32-10 stream, the fp32 Gumbel noise contract and the
-// bf16 store.  Functions are __host__ __device__ so that the noise contract
-// can also be exercised on the CPU.
+// bf16 store.  The Philox stream and the element helpers are __host__
+// __device__, so they can also be exercised on the CPU.
 //
 // Compile with -ffp-contract=off: the noise contract fixes every rounding, and
 // the only fused multiply-adds are the explicit __builtin_fmaf calls.
@@ -117,16 +117,6 @@ MASKGS_HD void stream_words(uint64_t q0, uint32_t step, uint32_t tensor_id, uint
     }
 }
 
-// ---------------------------------------------------------------------------
-// Noise contract.
-// Uniform: eps = (2*(x>>9) + 1) * 2^-24, exact, inside (0, 1).
-// Natural log ln_c: Cephes (S. L. Moshier) single-precision logarithm with a
-// fixed operation order: reduce x = 2^e * X with X in [sqrt(1/2), sqrt(2))
-// (the bit pattern 0x3F3504F3 of fp32 sqrt(1/2) splits the binade), f = X - 1,
-// ln(1+f) = f - f^2/2 + f^3 P(f) with Cephes' degree-8 P (Horner, fmaf), and
-// e*ln 2 added as 0.693359375*e plus -2.12194440e-4*e.
-// Gumbel (MaskLLM summary, section 3.4, Eq. 5): g = -ln_c(-ln_c(eps)).
-// ---------------------------------------------------------------------------
 MASKGS_HD float bits_to_f32(uint32_t u) {
 #if defined(__HIP_DEVICE_COMPILE__)
     return __uint_as_float(u);
@@ -147,51 +137,57 @@ MASKGS_HD uint32_t f32_to_bits(float f) {
 #endif
 }
 
-// ln_c on a pre-offset exponent/mantissa word ix = bits(x) - bits(sqrt(1/2)):
-// e = ix >> 23 (arithmetic), X = mantissa of ix re-based on sqrt(1/2).
-MASKGS_HD float ln_core(uint32_t ixu) {
-    const int32_t ix = static_cast<int32_t>(ixu);
-    const int32_t e = ix >> 23;  // exponent relative to [sqrt(1/2), sqrt(2))
-    const float X = bits_to_f32((ixu & 0x007FFFFFu) + 0x3F3504F3u);
-    const float f = X - 1.0f;
-    const float z = f * f;
-    float p = 7.0376836292e-2f;
-    p = __builtin_fmaf(p, f, -1.1514610310e-1f);
-    p = __builtin_fmaf(p, f, 1.1676998740e-1f);
-    p = __builtin_fmaf(p, f, -1.2420140846e-1f);
-    p = __builtin_fmaf(p, f, 1.4249322787e-1f);
-    p = __builtin_fmaf(p, f, -1.6668057665e-1f);
-    p = __builtin_fmaf(p, f, 2.0000714765e-1f);
-    p = __builtin_fmaf(p, f, -2.4999993993e-1f);
-    p = __builtin_fmaf(p, f, 3.3333331174e-1f);
-    float y = (p * f) * z;
-    const float fe = static_cast<float>(e);
-    y = __builtin_fmaf(fe, -2.12194440e-4f, y);
-    y = __builtin_fmaf(-0.5f, z, y);
-    float r = f + y;
-    r = __builtin_fmaf(fe, 0.693359375f, r);
+// ---------------------------------------------------------------------------
+// Noise contract: the Gumbel value of a Philox word (MaskLLM summary, section
+// 3.4, Eq. 5: g = -ln(-ln eps) for a uniform eps).
+// eps = k2 * 2^-24 with k2 = 2*(x >> 9) + 1, exact and inside (0, 1).  Below
+// 1/2 (side 0) v = k2, above (side 1) v = 2^24 - k2, the same integer for
+// 1 - eps; v in [2^b, 2^(b+1)).  g is a cubic in the offset d of v / 2^b from
+// the centre of its segment (32 per binade): the Taylor coefficients of
+// -ln(-ln eps) about that centre, one fp32 row (c0, c1, c2, c3) per
+// (side, binade, segment), generated into maskgs_gumbel_table.inc.  Within
+// 1.25 ulp of max(|g|, 1) of the exact value for all 2^23 uniforms.
+// ---------------------------------------------------------------------------
+constexpr int kGumbelRows = 2 * 24 * 32;
+
+// The coefficient table in device memory; kernels copy it into LDS (24 KB)
+// and evaluate the noise from there.
+static __constant__ __attribute__((aligned(16))) float kGumbelTable[kGumbelRows][4] = {
+#include "maskgs_gumbel_table.inc"
+};
+
+// Copies the table into LDS; all THREADS lanes of the workgroup call it and
+// pass a barrier before the first gumbel_lds.
+template <int THREADS>
+__device__ __forceinline__ void load_gumbel_table(float4 *lds) {
+    const float4 *src = reinterpret_cast<const float4 *>(kGumbelTable);
+    for (int i = threadIdx.x; i < kGumbelRows; i += THREADS) lds[i] = src[i];
+}
+
+// A plain register copy the compiler does not fold away.  The polynomial's
+// last fused multiply-add accumulates into the register that held c0, one of
+// the four registers of the LDS read; left there, every noise value (and the
+// logit built on it) kept a 4-aligned register slot, which took the 2:4
+// forward from 58 to 72 VGPRs and made the 4:8 kernels spill.
+__device__ __forceinline__ float fresh_reg(float x) {
+    float r;
+    asm("v_mov_b32 %0, %1" : "=v"(r) : "v"(x));
     return r;
 }
 
-MASKGS_HD float ln_contract(float x) { return ln_core(f32_to_bits(x) - 0x3F3504F3u); }
-
-MASKGS_HD float uniform_open(uint32_t x) {
-    return static_cast<float>(((x >> 9) << 1) | 1u) * 0x1p-24f;
+// g of the contract for Philox word x.  The row index is side * 768 + b * 32
+// + q, read off the exponent and the top 5 mantissa bits of fp32(v) (exact);
+// the low 18 mantissa bits give d = v / 2^b - 1 - (q + 1/2)/32, also exact.
+__device__ __forceinline__ float gumbel_lds(uint32_t x, const float4 *tab) {
+    const uint32_t k2 = (x >> 8) | 1u;
+    const uint32_t v = k2 < (1u << 24) - k2 ? k2 : (1u << 24) - k2;
+    const uint32_t f = f32_to_bits(static_cast<float>(v));
+    const uint32_t row = (f >> 18) - (127u << 5) + (k2 >> 23) * (24u * 32u);
+    const float d = bits_to_f32((f & 0x3FFFFu) | 0x3F800000u) - 1.015625f;
+    const float4 c = tab[row];
+    return fresh_reg(
+        __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(c.w, d, c.z), d, c.y), d, c.x));
 }
-
-// -ln_c(-ln_c(eps)), evaluated on exactly the same operands as the contract:
-//  - eps = (2k+1) * 2^-24 differs from the integer-valued float (2k+1) only in
-//    its exponent field (by 24), so ln_c(eps) reads the bits of (2k+1) with
-//    24 << 23 removed from the offset word;
-//  - t = -r1 flips only the sign bit of r1, which is the same as adding
-//    0x80000000 to its bit pattern.
-MASKGS_HD float neg_gumbel(uint32_t x) {  // returns -g
-    const float odd = static_cast<float>((x >> 8) | 1u);  // 2k+1, exact
-    const float r1 = ln_core(f32_to_bits(odd) - (0x3F3504F3u + (24u << 23)));
-    return ln_core(f32_to_bits(r1) + (0x80000000u - 0x3F3504F3u));
-}
-
-MASKGS_HD float gumbel(uint32_t x) { return -neg_gumbel(x); }
 
 // ---------------------------------------------------------------------------
 // Element access.

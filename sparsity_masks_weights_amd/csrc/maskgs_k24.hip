@@ -413,14 +413,15 @@ __device__ __forceinline__ void hard_pair(uint8_t *idx, uint8_t *bits, void *val
 }
 
 // Gumbel noise of a pair (section 3.4, Eq. 5): g_i of the contract for its
-// twelve candidates, +0 with the noise switched off.  It depends only on the
-// counters, so the kernels draw it right after requesting the pair's loads and
-// the memory latency passes under the noise arithmetic.  The noise flag is
-// uniform, so the twelve Gumbel evaluations form one straight-line block the
-// scheduler can interleave.
+// twelve candidates from the contract's coefficient table in LDS (gtab), +0
+// with the noise switched off.  It depends only on the counters, so the
+// kernels draw it right after requesting the pair's loads and the memory
+// latency passes under the noise arithmetic.  The noise flag is uniform, so
+// the twelve Gumbel evaluations form one straight-line block the scheduler can
+// interleave.
 template <int PHASE>
 __device__ __forceinline__ void pair_noise(const Geometry &g, const Noise &nz, int64_t p,
-                                           float (&g12)[12]) {
+                                           const float4 *gtab, float (&g12)[12]) {
     if (nz.no_noise) {
 #pragma unroll
         for (int i = 0; i < 12; ++i) g12[i] = 0.0f;
@@ -428,7 +429,7 @@ __device__ __forceinline__ void pair_noise(const Geometry &g, const Noise &nz, i
         uint32_t wd[12];
         pair_words<PHASE>(g, nz, p, wd);
 #pragma unroll
-        for (int i = 0; i < 12; ++i) g12[i] = -neg_gumbel(wd[i]);
+        for (int i = 0; i < 12; ++i) g12[i] = gumbel_lds(wd[i], gtab);
     }
 }
 
@@ -488,9 +489,12 @@ __device__ __forceinline__ void reduce_add(double v, double *dst) {
 // ---------------------------------------------------------------------------
 // Forward: W (.) M~, optional soft index and regulariser value.
 // ---------------------------------------------------------------------------
-template <int PHASE, typename WT, typename OT>
+template <int PHASE, typename WT, typename OT, bool YSAVE>
 __global__ __launch_bounds__(kThreads) void fwd24_kernel(FwdArgs a) {
-    __shared__ float4 stage[3 * kThreads];
+    __shared__ float4 stage[YSAVE ? 3 * kThreads : 1];
+    __shared__ float4 gtab[kGumbelRows];
+    load_gumbel_table<kThreads>(gtab);
+    __syncthreads();
     const bool hard = a.idx || a.bits || a.values || a.val_idx;
     const int64_t npairs = (a.g.nblocks + 1) >> 1;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
@@ -506,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void fwd24_kernel(FwdArgs a) {
             Io<WT>::load8(a.w, p, two, w, wd);
             load12(a.z, p, two, z);
             float g12[12];
-            pair_noise<PHASE>(a.g, a.nz, p, g12);
+            pair_noise<PHASE>(a.g, a.nz, p, gtab, g12);
             if (hard) {
                 // hard mask of the same logits (argmax of z, not of the sample)
                 hard_pair<WT>(a.idx, a.bits, a.values, a.val_idx, p, two, z, wd);
@@ -528,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void fwd24_kernel(FwdArgs a) {
             reg += static_cast<double>(racc);
             Io<OT>::store8(a.out, p, two, out);
         }
-        if (a.y) store12_wave(a.y, base, a.g.nblocks, y, stage);
+        if constexpr (YSAVE) store12_wave(a.y, base, a.g.nblocks, y, stage);
     }
     if (a.reg) reduce_add(reg, a.reg);
 }
@@ -541,6 +545,11 @@ __global__ __launch_bounds__(kThreads) void fwd24_kernel(FwdArgs a) {
 template <int PHASE, typename WT, typename GT, bool SAVED, bool ADAMW>
 __global__ __launch_bounds__(kThreads) void bwd24_kernel(BwdArgs a) {
     __shared__ float4 stage[3 * kThreads];
+    __shared__ float4 gtab[SAVED ? 1 : kGumbelRows];
+    if constexpr (!SAVED) {
+        load_gumbel_table<kThreads>(gtab);
+        __syncthreads();
+    }
     const int64_t npairs = (a.g.nblocks + 1) >> 1;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
     const double two_lambda = 2.0 * a.lambda;
@@ -559,7 +568,7 @@ __global__ __launch_bounds__(kThreads) void bwd24_kernel(BwdArgs a) {
             } else {
                 float z[12], g12[12];
                 load12(a.z, p, two, z);
-                pair_noise<PHASE>(a.g, a.nz, p, g12);
+                pair_noise<PHASE>(a.g, a.nz, p, gtab, g12);
                 pair_sample(a.nz, z, g12, y, hm);
             }
             float prev[12];
@@ -630,6 +639,11 @@ __global__ __launch_bounds__(kThreads) void bwd24_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 template <int PHASE, typename WT, bool SAVED>
 __global__ __launch_bounds__(kThreads) void reg24_kernel(RegArgs a) {
+    __shared__ float4 gtab[SAVED ? 1 : kGumbelRows];
+    if constexpr (!SAVED) {
+        load_gumbel_table<kThreads>(gtab);
+        __syncthreads();
+    }
     const int64_t npairs = (a.g.nblocks + 1) >> 1;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
     double reg = 0.0;
@@ -644,7 +658,7 @@ __global__ __launch_bounds__(kThreads) void reg24_kernel(RegArgs a) {
         } else {
             float z[12], g12[12];
             load12(a.z, p, two, z);
-            pair_noise<PHASE>(a.g, a.nz, p, g12);
+            pair_noise<PHASE>(a.g, a.nz, p, gtab, g12);
             pair_sample(a.nz, z, g12, y, hm);
         }
         float racc = 0.0f;
@@ -824,6 +838,11 @@ __device__ __forceinline__ void stats_flush(double (&v)[5], maskgs_stats *st) {
 
 template <int PHASE, typename WT, bool SAMPLED>
 __global__ __launch_bounds__(kThreads) void stats24_kernel(StatsArgs a) {
+    __shared__ float4 gtab[SAMPLED ? kGumbelRows : 1];
+    if constexpr (SAMPLED) {
+        load_gumbel_table<kThreads>(gtab);
+        __syncthreads();
+    }
     const int64_t npairs = (a.g.nblocks + 1) >> 1;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
     double acc[5] = {0.0, 0.0, 0.0, 0.0, 0.0};  // changed, max_prob, kept, magnitude, grad^2
@@ -842,7 +861,7 @@ __global__ __launch_bounds__(kThreads) void stats24_kernel(StatsArgs a) {
         int k0, k1;
         if (SAMPLED) {
             float a12[12], g12[12];
-            pair_noise<PHASE>(a.g, a.nz, p, g12);
+            pair_noise<PHASE>(a.g, a.nz, p, gtab, g12);
             pair_logits(a.nz, z, g12, a12);
             k0 = first_argmax6(a12);
             k1 = first_argmax6(a12 + 6);
@@ -894,17 +913,17 @@ constexpr int kStatsWgPerCU = 2;
 
 int phase_of(uint64_t block_offset) { return (block_offset & 1u) ? 2 : 0; }
 
-template <int PHASE>
+template <int PHASE, bool YSAVE>
 hipError_t fwd24_dispatch(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype o_dt,
                           hipStream_t s) {
     const int64_t np = (a.g.nblocks + 1) >> 1;
     if (w_dt == MASKGS_BF16 && o_dt == MASKGS_BF16)
-        return go(fwd24_kernel<PHASE, bf16_t, bf16_t>, a, np, s);
+        return go(fwd24_kernel<PHASE, bf16_t, bf16_t, YSAVE>, a, np, s);
     if (w_dt == MASKGS_BF16 && o_dt == MASKGS_F32)
-        return go(fwd24_kernel<PHASE, bf16_t, float>, a, np, s);
+        return go(fwd24_kernel<PHASE, bf16_t, float, YSAVE>, a, np, s);
     if (w_dt == MASKGS_F32 && o_dt == MASKGS_BF16)
-        return go(fwd24_kernel<PHASE, float, bf16_t>, a, np, s);
-    return go(fwd24_kernel<PHASE, float, float>, a, np, s);
+        return go(fwd24_kernel<PHASE, float, bf16_t, YSAVE>, a, np, s);
+    return go(fwd24_kernel<PHASE, float, float, YSAVE>, a, np, s);
 }
 
 template <int PHASE, bool SAVED, bool ADAMW>
@@ -939,8 +958,11 @@ hipError_t reg24_dispatch(const RegArgs &a, maskgs_dtype w_dt, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd24(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype out_dt, hipStream_t s) {
-    return phase_of(a.g.block_offset) == 0 ? fwd24_dispatch<0>(a, w_dt, out_dt, s)
-                                           : fwd24_dispatch<2>(a, w_dt, out_dt, s);
+    const bool even = phase_of(a.g.block_offset) == 0;
+    if (a.y) return even ? fwd24_dispatch<0, true>(a, w_dt, out_dt, s)
+                         : fwd24_dispatch<2, true>(a, w_dt, out_dt, s);
+    return even ? fwd24_dispatch<0, false>(a, w_dt, out_dt, s)
+                : fwd24_dispatch<2, false>(a, w_dt, out_dt, s);
 }
 
 hipError_t launch_bwd24(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, hipStream_t s) {

@@ -1,7 +1,10 @@
 // maskgs_k48.hip -- 4:8 kernels of libmaskgs for gfx950.
 //
-// Work item = one block per lane (70 candidates, K = C(8,4)); a workgroup is
-// one wave and walks tiles of 64 consecutive blocks.  Logit-sized streams
+// Work item = one block per lane (70 candidates, K = C(8,4)); each wave walks
+// tiles of 64 consecutive blocks, its tiles staged in its own slice of the
+// workgroup's LDS.  The kernels that draw noise run several waves per
+// workgroup, which share one LDS copy of the noise contract's coefficient
+// table; the others run one wave per workgroup.  Logit-sized streams
 // (280 B per block) always cross HBM as fully coalesced 16 B-per-lane copies
 // through LDS (stores non-temporal).  Two kernel shapes:
 //  - noise kernels (forward; backward and regulariser that recompute the soft
@@ -30,6 +33,9 @@ namespace maskgs {
 namespace {
 
 constexpr int kWave = 64;
+
+// Lane within the wave (workgroups of the noise kernels hold several waves).
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 typedef float v4f48 __attribute__((ext_vector_type(4)));
 
 // Non-temporal 16-byte store: the logit-sized outputs (soft index, gradient,
@@ -52,6 +58,20 @@ constexpr int kHalf = 32;  // blocks staged per LDS round
 constexpr int kWgPerCU = 96;
 constexpr int kWgPerCUStream = 4096;
 using C48 = Cands<4, 8>;
+
+// Waves per workgroup of the kernels that draw noise.  Their workgroup holds
+// one 24 KB copy of the noise coefficient table next to each wave's LDS
+// slice, and the grid holds the workgroups that fit the CUs at once (each
+// wave then walks its share of the tiles):
+//  - forward and regulariser (8960 B slice per wave): 4 waves, 2 workgroups
+//    per CU (120.8 KB), the 2 waves per SIMD their 170-240 registers allow;
+//  - backward recomputing the soft index (17920 B tile per wave): 7 waves,
+//    one workgroup per CU (150 KB); 3 with accumulation (a second tile);
+//  - the sampled diagnostics (17920 B tile): 7 waves, one per CU.
+constexpr int kNoiseWaves = 4;
+constexpr int kNoiseWgPerCU = 2;
+constexpr int bwd48_waves(bool saved, bool acc) { return saved ? 1 : (acc ? 3 : 7); }
+constexpr int kStatsNoiseWaves = 7;
 
 // ---------------------------------------------------------------------------
 // Tile transfers through LDS.  Tile = blocks [b0, b0+nb), b0 a multiple of 64,
@@ -76,7 +96,7 @@ __device__ __forceinline__ __attribute__((address_space(3))) void *lds_addr(cons
 // registers stage the data.  An odd float pair at the end is moved by lane 0.
 // Follow with lds_fill_wait() and a barrier before reading the LDS copy.
 __device__ __forceinline__ void lds_fill(const float *src, float *lds, int nf) {
-    const int lane = threadIdx.x;
+    const int lane = lane_id();
     const int n4 = nf >> 2;
     for (int k = 0; k * kWave < n4; ++k) {
         const int i = k * kWave + lane;
@@ -92,6 +112,16 @@ __device__ __forceinline__ void lds_fill(const float *src, float *lds, int nf) {
 // loads of lds_fill among them.
 __device__ __forceinline__ void lds_fill_wait() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Orders a wave's LDS writes before its later LDS reads (and its reads before
+// later writes).  Every LDS slice below belongs to one wave, so no other wave
+// of the workgroup takes part: a wave's LDS operations complete in order, and
+// this only keeps the compiler from moving accesses across it.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // A tile's worth of floats held in registers between an LDS read and the
 // global stores: lane l keeps float4 numbers 64k+l (and lane 0 the odd float
 // pair at the end).  CAP is the float4 size of the LDS buffer.
@@ -104,7 +134,7 @@ struct TileRegs {
     // Reads the LDS buffer.  Every lane reads (a clamped, in-bounds index), so
     // the array stays in registers; only the stores below are predicated.
     __device__ __forceinline__ void gather(const float *lds, int nf) {
-        const int lane = threadIdx.x;
+        const int lane = lane_id();
 #pragma unroll
         for (int k = 0; k < kRounds; ++k) {
             const int i = k * kWave + lane;
@@ -115,7 +145,7 @@ struct TileRegs {
     }
     // Writes nf floats to dst (16-byte aligned).
     __device__ __forceinline__ void scatter(float *dst, int nf) const {
-        const int lane = threadIdx.x;
+        const int lane = lane_id();
         const int n4 = nf >> 2;
 #pragma unroll
         for (int k = 0; k < kRounds; ++k) {
@@ -129,13 +159,13 @@ struct TileRegs {
 template <bool ADD>
 __device__ __forceinline__ void tile_in(const float *g, int64_t b0, int nb, float *stage,
                                         float (&v)[kK]) {
-    const int lane = threadIdx.x;
+    const int lane = lane_id();
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int cnt = half_count(nb, h);
         lds_fill(g + (b0 + h * kHalf) * kK, stage, cnt * kK);
         lds_fill_wait();
-        __syncthreads();
+        wave_sync();
         const int j = lane - h * kHalf;
         if (j >= 0 && j < cnt) {
             const float2 *row = reinterpret_cast<const float2 *>(stage) + j * (kK / 2);
@@ -151,13 +181,13 @@ __device__ __forceinline__ void tile_in(const float *g, int64_t b0, int nb, floa
                 }
             }
         }
-        __syncthreads();
+        wave_sync();
     }
 }
 
 __device__ __forceinline__ void tile_out(float *g, int64_t b0, int nb, float *stage,
                                          const float (&v)[kK]) {
-    const int lane = threadIdx.x;
+    const int lane = lane_id();
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int cnt = half_count(nb, h);
@@ -167,14 +197,14 @@ __device__ __forceinline__ void tile_out(float *g, int64_t b0, int nb, float *st
 #pragma unroll
             for (int t = 0; t < kK / 2; ++t) row[t] = make_float2(v[2 * t], v[2 * t + 1]);
         }
-        __syncthreads();
+        wave_sync();
         float *dst = g + (b0 + h * kHalf) * kK;
         const int nf = cnt * kK, n4 = nf >> 2;
         for (int i = lane; i < n4; i += kWave)
             nt_store4(reinterpret_cast<float4 *>(dst) + i, reinterpret_cast<const float4 *>(stage)[i]);
         if ((nf & 3) && lane == 0)
             reinterpret_cast<float2 *>(dst)[2 * n4] = reinterpret_cast<const float2 *>(stage)[2 * n4];
-        __syncthreads();
+        wave_sync();
     }
 }
 
@@ -258,7 +288,7 @@ __device__ __forceinline__ void philox_call(uint64_t q, uint32_t step, uint32_t 
 
 // v: logits z on entry, a_i = fp32(fp32(kappa z_i + g_i) * fp32(1/tau)) on exit.
 __device__ __forceinline__ void logits70(float (&v)[kK], uint64_t gb, const Geometry &g,
-                                         const Noise &nz) {
+                                         const Noise &nz, const float4 *gtab) {
     if (nz.no_noise) {
 #pragma unroll
         for (int i = 0; i < kK; ++i) v[i] = __builtin_fmaf(nz.kappa, v[i], 0.0f) * nz.tau_inv;
@@ -279,7 +309,7 @@ __device__ __forceinline__ void logits70(float (&v)[kK], uint64_t gb, const Geom
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int i = 4 * c + u;
-            if (i < kK) v[i] = __builtin_fmaf(nz.kappa, v[i], gumbel(wd[u])) * nz.tau_inv;
+            if (i < kK) v[i] = __builtin_fmaf(nz.kappa, v[i], gumbel_lds(wd[u], gtab)) * nz.tau_inv;
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) prev[u] = cur[u];
@@ -372,7 +402,7 @@ __device__ __forceinline__ void applied_mask8(const float (&y)[kK], uint32_t hm,
 __device__ __forceinline__ void reduce_add_wave(double v, double *dst) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    if (threadIdx.x == 0) atomicAdd(dst, v);
+    if (lane_id() == 0) atomicAdd(dst, v);
 }
 
 __device__ __forceinline__ int64_t tile_count(int64_t nblocks) {
@@ -383,13 +413,18 @@ __device__ __forceinline__ int64_t tile_count(int64_t nblocks) {
 // Forward (noise kernel, registers).
 // ---------------------------------------------------------------------------
 template <typename WT, typename OT, bool HARD, bool SAMPLE>
-__global__ __launch_bounds__(kWave) void fwd48_kernel(FwdArgs a) {
-    __shared__ float4 stage4[kHalf * kK / 4];
-    float *stage = reinterpret_cast<float *>(stage4);
-    const int lane = threadIdx.x;
+__global__ __launch_bounds__(kWave * kNoiseWaves) void fwd48_kernel(FwdArgs a) {
+    __shared__ float4 stage4[kNoiseWaves][kHalf * kK / 4];
+    __shared__ float4 gtab[kGumbelRows];
+    load_gumbel_table<kWave * kNoiseWaves>(gtab);
+    __syncthreads();
+    const int wv = threadIdx.x / kWave;
+    float *stage = reinterpret_cast<float *>(stage4[wv]);
+    const int lane = lane_id();
     const int64_t ntiles = tile_count(a.g.nblocks);
     double reg = 0.0;
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    for (int64_t tile = static_cast<int64_t>(blockIdx.x) * kNoiseWaves + wv; tile < ntiles;
+         tile += static_cast<int64_t>(gridDim.x) * kNoiseWaves) {
         const int64_t b0 = tile * kWave;
         const int nb = static_cast<int>(a.g.nblocks - b0 < kWave ? a.g.nblocks - b0 : kWave);
         const int64_t b = b0 + lane;
@@ -402,7 +437,7 @@ __global__ __launch_bounds__(kWave) void fwd48_kernel(FwdArgs a) {
                 if (a.idx) a.idx[b] = static_cast<uint8_t>(key >> 8);
                 if (a.bits) a.bits[b] = static_cast<uint8_t>(key);
             }
-            logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz);
+            logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz, gtab);
             uint32_t hm = 0u;
             softmax70<SAMPLE>(v, &hm);
             float m[8], w[8], out[8];
@@ -426,20 +461,25 @@ __global__ __launch_bounds__(kWave) void fwd48_kernel(FwdArgs a) {
 // Regulariser value (section 3.4, Eq. 8), recomputing the soft index.
 // ---------------------------------------------------------------------------
 template <typename WT, bool SAMPLE>
-__global__ __launch_bounds__(kWave) void reg48_noise_kernel(RegArgs a) {
-    __shared__ float4 stage4[kHalf * kK / 4];
-    float *stage = reinterpret_cast<float *>(stage4);
-    const int lane = threadIdx.x;
+__global__ __launch_bounds__(kWave * kNoiseWaves) void reg48_noise_kernel(RegArgs a) {
+    __shared__ float4 stage4[kNoiseWaves][kHalf * kK / 4];
+    __shared__ float4 gtab[kGumbelRows];
+    load_gumbel_table<kWave * kNoiseWaves>(gtab);
+    __syncthreads();
+    const int wv = threadIdx.x / kWave;
+    float *stage = reinterpret_cast<float *>(stage4[wv]);
+    const int lane = lane_id();
     const int64_t ntiles = tile_count(a.g.nblocks);
     double reg = 0.0;
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    for (int64_t tile = static_cast<int64_t>(blockIdx.x) * kNoiseWaves + wv; tile < ntiles;
+         tile += static_cast<int64_t>(gridDim.x) * kNoiseWaves) {
         const int64_t b0 = tile * kWave;
         const int nb = static_cast<int>(a.g.nblocks - b0 < kWave ? a.g.nblocks - b0 : kWave);
         const int64_t b = b0 + lane;
         float v[kK];
         tile_in<false>(a.z, b0, nb, stage, v);
         if (lane < nb) {
-            logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz);
+            logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz, gtab);
             uint32_t hm = 0u;
             softmax70<SAMPLE>(v, &hm);
             float m[8], w[8];
@@ -508,20 +548,28 @@ __device__ __forceinline__ void row_soft_mask_f64(const float *row, double (&md)
 // dz_i = (kappa/tau) y_i (dy_i - s), dy_i = sum_{j in S_i} dm_j, with
 // s = sum_i y_i dy_i / sum_i y_i.
 template <typename WT, typename GT, bool SAVED, bool ACC, bool ADAMW, bool SAMPLE>
-__global__ __launch_bounds__(kWave) void bwd48_kernel(BwdArgs a) {
-    __shared__ float4 tile4[kWave * kK / 4];
-    __shared__ float4 prev4[ACC ? kWave * kK / 4 : 1];
-    float *tl = reinterpret_cast<float *>(tile4);
-    const float *pv = reinterpret_cast<const float *>(prev4);
-    const int lane = threadIdx.x;
+__global__ __launch_bounds__(kWave * bwd48_waves(SAVED, ACC)) void bwd48_kernel(BwdArgs a) {
+    constexpr int W = bwd48_waves(SAVED, ACC);
+    __shared__ float4 tile4[W][kWave * kK / 4];
+    __shared__ float4 prev4[ACC ? W : 1][ACC ? kWave * kK / 4 : 1];
+    __shared__ float4 gtab[SAVED ? 1 : kGumbelRows];
+    if constexpr (!SAVED) {
+        load_gumbel_table<kWave * W>(gtab);
+        __syncthreads();
+    }
+    const int wv = threadIdx.x / kWave;
+    float *tl = reinterpret_cast<float *>(tile4[wv]);
+    const float *pv = reinterpret_cast<const float *>(prev4[ACC ? wv : 0]);
+    const int lane = lane_id();
     const int64_t ntiles = tile_count(a.g.nblocks);
     const double two_lambda = 2.0 * a.lambda;
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    for (int64_t tile = static_cast<int64_t>(blockIdx.x) * W + wv; tile < ntiles;
+         tile += static_cast<int64_t>(gridDim.x) * W) {
         const int64_t b0 = tile * kWave;
         const int nb = static_cast<int>(a.g.nblocks - b0 < kWave ? a.g.nblocks - b0 : kWave);
         const int64_t b = b0 + lane;
         tile_copy_in(SAVED ? a.y : a.z, b0, nb, tl);
-        if (ACC) tile_copy_in(a.dz, b0, nb, reinterpret_cast<float *>(prev4));
+        if (ACC) tile_copy_in(a.dz, b0, nb, reinterpret_cast<float *>(prev4[ACC ? wv : 0]));
         // the block's weights and upstream gradient are requested with the tile,
         // so one wait covers all of them
         float w[8], G[8];
@@ -530,7 +578,7 @@ __global__ __launch_bounds__(kWave) void bwd48_kernel(BwdArgs a) {
             Io8<GT>::load(a.dout, b, G);
         }
         lds_fill_wait();
-        __syncthreads();
+        wave_sync();
         float *row = tl + lane * kK;
         if (lane < nb) {
             uint32_t hm = 0u;
@@ -538,7 +586,7 @@ __global__ __launch_bounds__(kWave) void bwd48_kernel(BwdArgs a) {
                 float v[kK];
 #pragma unroll
                 for (int i = 0; i < kK; ++i) v[i] = row[i];
-                logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz);
+                logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz, gtab);
                 softmax70<SAMPLE>(v, &hm);
 #pragma unroll
                 for (int i = 0; i < kK; ++i) row[i] = v[i];
@@ -591,7 +639,7 @@ __global__ __launch_bounds__(kWave) void bwd48_kernel(BwdArgs a) {
                 }
             }
         }
-        __syncthreads();
+        wave_sync();
         if (ADAMW) {
             // the gradient tile in LDS feeds the AdamW update of the same logits
             adamw_span<kWave, kWave * kK / 4, 6>(a.zu + b0 * kK, a.m1 + b0 * kK, a.m2 + b0 * kK,
@@ -599,7 +647,7 @@ __global__ __launch_bounds__(kWave) void bwd48_kernel(BwdArgs a) {
         } else {
             tile_copy_out(a.dz, b0, nb, tl);
         }
-        __syncthreads();
+        wave_sync();
     }
 }
 
@@ -738,17 +786,26 @@ __global__ __launch_bounds__(kWave) void prior48_kernel(PriorArgs a) {
 // per wave.
 // ---------------------------------------------------------------------------
 template <typename WT, bool SAMPLED>
-__global__ __launch_bounds__(kWave) void stats48_kernel(StatsArgs a) {
-    __shared__ float4 tile4[kWave * kK / 4];
-    const float *tl = reinterpret_cast<const float *>(tile4);
-    const int lane = threadIdx.x;
+__global__ __launch_bounds__(kWave * (SAMPLED ? kStatsNoiseWaves : 1)) void stats48_kernel(
+    StatsArgs a) {
+    constexpr int W = SAMPLED ? kStatsNoiseWaves : 1;
+    __shared__ float4 tile4[W][kWave * kK / 4];
+    __shared__ float4 gtab[SAMPLED ? kGumbelRows : 1];
+    if constexpr (SAMPLED) {
+        load_gumbel_table<kWave * W>(gtab);
+        __syncthreads();
+    }
+    const int wv = threadIdx.x / kWave;
+    const float *tl = reinterpret_cast<const float *>(tile4[wv]);
+    const int lane = lane_id();
     const int64_t ntiles = tile_count(a.g.nblocks);
     double acc[5] = {0.0, 0.0, 0.0, 0.0, 0.0};  // changed, max_prob, kept, magnitude, grad^2
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    for (int64_t tile = static_cast<int64_t>(blockIdx.x) * W + wv; tile < ntiles;
+         tile += static_cast<int64_t>(gridDim.x) * W) {
         const int64_t b0 = tile * kWave;
         const int nb = static_cast<int>(a.g.nblocks - b0 < kWave ? a.g.nblocks - b0 : kWave);
         const int64_t b = b0 + lane;
-        tile_copy_in(a.z, b0, nb, reinterpret_cast<float *>(tile4));
+        tile_copy_in(a.z, b0, nb, reinterpret_cast<float *>(tile4[wv]));
         // the block's weights and reference mask are requested with the tile,
         // so the tile's wait covers them
         float w[8];
@@ -762,7 +819,7 @@ __global__ __launch_bounds__(kWave) void stats48_kernel(StatsArgs a) {
             if (a.ref_bits) rb = a.ref_bits[b];
         }
         lds_fill_wait();
-        __syncthreads();
+        wave_sync();
         if (lane < nb) {
             const float *row = tl + lane * kK;
             uint32_t key;
@@ -770,7 +827,7 @@ __global__ __launch_bounds__(kWave) void stats48_kernel(StatsArgs a) {
                 float v[kK];
 #pragma unroll
                 for (int i = 0; i < kK; ++i) v[i] = row[i];
-                logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz);
+                logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz, gtab);
                 key = argmax_key70(v);
             } else {
                 key = argmax_key70(row);
@@ -819,7 +876,7 @@ __global__ __launch_bounds__(kWave) void stats48_kernel(StatsArgs a) {
                 acc[4] += static_cast<double>(d.x) * d.x + static_cast<double>(d.y) * d.y;
             }
         }
-        __syncthreads();
+        wave_sync();
     }
 #pragma unroll
     for (int k = 0; k < 5; ++k)
@@ -836,7 +893,7 @@ __global__ __launch_bounds__(kWave) void stats48_kernel(StatsArgs a) {
             atomicAdd(&st->magnitude_l1, acc[3]);
         }
         if (acc[4] != 0.0) atomicAdd(&st->grad_sq, acc[4]);
-        if (blockIdx.x == 0)
+        if (blockIdx.x == 0 && wv == 0)
             atomicAdd(reinterpret_cast<unsigned long long *>(&st->blocks),
                       static_cast<unsigned long long>(a.g.nblocks));
     }
@@ -850,16 +907,31 @@ hipError_t go(Kern kernel, const A &args, int64_t nblocks, hipStream_t s,
     return hipGetLastError();
 }
 
+// Launch of a kernel with `waves` waves per workgroup, each wave walking its
+// own tiles: at most wg_per_cu workgroups per CU, and no more than the tiles
+// need.
+template <typename Kern, typename A>
+hipError_t go_waves(Kern kernel, const A &args, int64_t nblocks, int waves, int wg_per_cu,
+                    hipStream_t s) {
+    const int64_t tiles = (nblocks + kWave - 1) / kWave;
+    const unsigned grid = grid_for((tiles + waves - 1) / waves, 1, wg_per_cu);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kWave * waves), 0, s, args);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 template <bool HARD, bool SAMPLE>
 hipError_t fwd48_dispatch(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype out_dt, hipStream_t s) {
     const int64_t n = a.g.nblocks;
+    const int w = kNoiseWaves, c = kNoiseWgPerCU;
     if (w_dt == MASKGS_BF16 && out_dt == MASKGS_BF16)
-        return go(fwd48_kernel<bf16_t, bf16_t, HARD, SAMPLE>, a, n, s);
-    if (w_dt == MASKGS_BF16) return go(fwd48_kernel<bf16_t, float, HARD, SAMPLE>, a, n, s);
-    if (out_dt == MASKGS_BF16) return go(fwd48_kernel<float, bf16_t, HARD, SAMPLE>, a, n, s);
-    return go(fwd48_kernel<float, float, HARD, SAMPLE>, a, n, s);
+        return go_waves(fwd48_kernel<bf16_t, bf16_t, HARD, SAMPLE>, a, n, w, c, s);
+    if (w_dt == MASKGS_BF16)
+        return go_waves(fwd48_kernel<bf16_t, float, HARD, SAMPLE>, a, n, w, c, s);
+    if (out_dt == MASKGS_BF16)
+        return go_waves(fwd48_kernel<float, bf16_t, HARD, SAMPLE>, a, n, w, c, s);
+    return go_waves(fwd48_kernel<float, float, HARD, SAMPLE>, a, n, w, c, s);
 }
 
 hipError_t launch_fwd48(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype out_dt, hipStream_t s) {
@@ -875,12 +947,15 @@ template <bool SAVED, bool ACC, bool ADAMW, bool SAMPLE>
 hipError_t bwd48_dispatch(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, hipStream_t s) {
     const int64_t n = a.g.nblocks;
     const bool wb = w_dt == MASKGS_BF16, gb = g_dt == MASKGS_BF16;
-    // the soft-index-recomputing backward draws noise and takes the smaller cap
-    const int c = SAVED ? kWgPerCUStream : kWgPerCU;
-    if (wb && gb) return go(bwd48_kernel<bf16_t, bf16_t, SAVED, ACC, ADAMW, SAMPLE>, a, n, s, c);
-    if (wb) return go(bwd48_kernel<bf16_t, float, SAVED, ACC, ADAMW, SAMPLE>, a, n, s, c);
-    if (gb) return go(bwd48_kernel<float, bf16_t, SAVED, ACC, ADAMW, SAMPLE>, a, n, s, c);
-    return go(bwd48_kernel<float, float, SAVED, ACC, ADAMW, SAMPLE>, a, n, s, c);
+    // from a saved soft index: one wave per workgroup, one tile each; the
+    // recomputing backward draws noise: multi-wave workgroups, one per CU
+    constexpr int w = bwd48_waves(SAVED, ACC);
+    const int c = SAVED ? kWgPerCUStream : 1;
+    if (wb && gb)
+        return go_waves(bwd48_kernel<bf16_t, bf16_t, SAVED, ACC, ADAMW, SAMPLE>, a, n, w, c, s);
+    if (wb) return go_waves(bwd48_kernel<bf16_t, float, SAVED, ACC, ADAMW, SAMPLE>, a, n, w, c, s);
+    if (gb) return go_waves(bwd48_kernel<float, bf16_t, SAVED, ACC, ADAMW, SAMPLE>, a, n, w, c, s);
+    return go_waves(bwd48_kernel<float, float, SAVED, ACC, ADAMW, SAMPLE>, a, n, w, c, s);
 }
 
 hipError_t launch_bwd48(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, hipStream_t s) {
@@ -904,11 +979,12 @@ hipError_t launch_reg48(const RegArgs &a, maskgs_dtype w_dt, hipStream_t s) {
     const int64_t n = a.g.nblocks;
     const bool bf = w_dt == MASKGS_BF16;
     if (a.y) return bf ? go(reg48_saved_kernel<bf16_t>, a, n, s) : go(reg48_saved_kernel<float>, a, n, s);
+    const int w = kNoiseWaves, c = kNoiseWgPerCU;
     if (a.nz.hard_sample)
-        return bf ? go(reg48_noise_kernel<bf16_t, true>, a, n, s)
-                  : go(reg48_noise_kernel<float, true>, a, n, s);
-    return bf ? go(reg48_noise_kernel<bf16_t, false>, a, n, s)
-              : go(reg48_noise_kernel<float, false>, a, n, s);
+        return bf ? go_waves(reg48_noise_kernel<bf16_t, true>, a, n, w, c, s)
+                  : go_waves(reg48_noise_kernel<float, true>, a, n, w, c, s);
+    return bf ? go_waves(reg48_noise_kernel<bf16_t, false>, a, n, w, c, s)
+              : go_waves(reg48_noise_kernel<float, false>, a, n, w, c, s);
 }
 
 hipError_t launch_hard48(const HardArgs &a, hipStream_t s) {
@@ -932,9 +1008,10 @@ constexpr int kStatsWgPerCU = 8;
 hipError_t launch_stats48(const StatsArgs &a, bool sampled, maskgs_dtype w_dt, hipStream_t s) {
     const int64_t n = a.g.nblocks;
     const int c = kStatsWgPerCU;
-    if (sampled)
-        return w_dt == MASKGS_F32 ? go(stats48_kernel<float, true>, a, n, s, c)
-                                  : go(stats48_kernel<bf16_t, true>, a, n, s, c);
+    if (sampled)  // draws noise: multi-wave workgroups, one per CU
+        return w_dt == MASKGS_F32
+                   ? go_waves(stats48_kernel<float, true>, a, n, kStatsNoiseWaves, 1, s)
+                   : go_waves(stats48_kernel<bf16_t, true>, a, n, kStatsNoiseWaves, 1, s);
     return w_dt == MASKGS_F32 ? go(stats48_kernel<float, false>, a, n, s, c)
                               : go(stats48_kernel<bf16_t, false>, a, n, s, c);
 }

@@ -15,6 +15,7 @@
 #include <cstdint>
 
 #include "maskgs_device.hpp"
+#include "maskgs_launch.hpp"
 #include "maskpro_launch.hpp"
 
 namespace maskgs {
@@ -135,11 +136,11 @@ struct Elem<bf16_t> {
 // The draw: keys a_j = fp32(pi_j + g_j) (g_j from Philox word gb*M + j), then
 // N rounds of "first largest key among the positions not yet drawn" (strict
 // '>' from the lowest position, so ties and NaN keys go to the lower one).
-// pi_j - (-g_j) is bit-identical to pi_j + g_j.
+// gtab: the noise contract's coefficient table in LDS.
 // ---------------------------------------------------------------------------
 template <int N, int M>
 __device__ __forceinline__ uint32_t draw(const float (&p)[M], uint64_t gb, const MpArgs &a,
-                                         int (&ord)[N]) {
+                                         const float4 *gtab, int (&ord)[N]) {
     float key[M];
     if (a.no_noise) {
 #pragma unroll
@@ -149,7 +150,7 @@ __device__ __forceinline__ uint32_t draw(const float (&p)[M], uint64_t gb, const
         stream_words<M, 0>(gb * static_cast<uint64_t>(M / 4), a.step, a.tensor_id, a.k0, a.k1,
                            wd);
 #pragma unroll
-        for (int j = 0; j < M; ++j) key[j] = p[j] - neg_gumbel(wd[j]);
+        for (int j = 0; j < M; ++j) key[j] = p[j] + gumbel_lds(wd[j], gtab);
     }
     uint32_t taken = 0;
 #pragma unroll
@@ -182,6 +183,9 @@ __device__ __forceinline__ uint32_t pack_order(const int (&ord)[N]) {
 // ---------------------------------------------------------------------------
 template <int N, int M, typename WT, typename OT>
 __global__ __launch_bounds__(kThreads) void mp_fwd_kernel(MpArgs a) {
+    __shared__ float4 gtab[kGumbelRows];
+    load_gumbel_table<kThreads>(gtab);
+    __syncthreads();
     // grid-stride over workgroup-sized spans of blocks (the span base is
     // uniform, so every lane of a wave reaches the cross-lane swap below)
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
@@ -194,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void mp_fwd_kernel(MpArgs a) {
             float p[M];
             BlockIo<float, M>::load(a.pi, b, p);
             int ord[N];
-            keep = draw<N, M>(p, a.block_offset + static_cast<uint64_t>(b), a, ord);
+            keep = draw<N, M>(p, a.block_offset + static_cast<uint64_t>(b), a, gtab, ord);
             if (a.out) {
                 uint32_t r[M], o[M];
                 BlockIo<WT, M>::load_raw(a.w, b, r);
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void mp_fwd_kernel(MpArgs a) {
 // of one ulp of 1.  dpi = A * acc (+ dpi when accumulating).
 // ---------------------------------------------------------------------------
 template <int N, int M, bool ORDER_IN>
-__device__ __forceinline__ void mp_bwd_block(const MpArgs &a, int64_t b) {
+__device__ __forceinline__ void mp_bwd_block(const MpArgs &a, int64_t b, const float4 *gtab) {
     float q[M];
     BlockIo<float, M>::load(a.pi, b, q);
     int ord[N];
@@ -251,7 +255,7 @@ __device__ __forceinline__ void mp_bwd_block(const MpArgs &a, int64_t b) {
 #pragma unroll
         for (int k = 0; k < N; ++k) ord[k] = (v >> (kBits * k)) & ((1u << kBits) - 1u);
     } else {
-        draw<N, M>(q, a.block_offset + static_cast<uint64_t>(b), a, ord);
+        draw<N, M>(q, a.block_offset + static_cast<uint64_t>(b), a, gtab, ord);
     }
     float acc[M];
 #pragma unroll
@@ -295,10 +299,15 @@ __device__ __forceinline__ void mp_bwd_block(const MpArgs &a, int64_t b) {
 
 template <int N, int M, bool ORDER_IN>
 __global__ __launch_bounds__(kThreads) void mp_bwd_kernel(MpArgs a) {
+    __shared__ float4 gtab[ORDER_IN ? 1 : kGumbelRows];
+    if constexpr (!ORDER_IN) {
+        load_gumbel_table<kThreads>(gtab);
+        __syncthreads();
+    }
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
     for (int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; b < a.nblocks;
          b += stride)
-        mp_bwd_block<N, M, ORDER_IN>(a, b);
+        mp_bwd_block<N, M, ORDER_IN>(a, b, gtab);
 }
 
 // ---------------------------------------------------------------------------
@@ -353,13 +362,25 @@ unsigned blocks_for(int64_t nblocks) {
     return static_cast<unsigned>(want < (INT64_C(1) << 20) ? want : (INT64_C(1) << 20));
 }
 
+// The kernels that draw noise first copy the 24 KB coefficient table into
+// LDS, so their grids stop at the workgroups that fit the CUs at once (six of
+// 256 lanes per CU by LDS) and loop over the rest: the table is read once per
+// resident workgroup instead of once per 256 blocks.
+constexpr int kNoiseWgPerCU = 6;
+unsigned noise_blocks_for(int64_t nblocks) {
+    const int64_t want = (nblocks + kThreads - 1) / kThreads;
+    const int64_t cap = static_cast<int64_t>(device_cu_count()) * kNoiseWgPerCU;
+    const int64_t g = want < cap ? want : cap;
+    return static_cast<unsigned>(g < 1 ? 1 : g);
+}
+
 template <int N, int M, typename WT>
 hipError_t fwd_out(const MpArgs &a, maskgs_dtype out_dt, hipStream_t s) {
     if (out_dt == MASKGS_BF16)
-        hipLaunchKernelGGL((mp_fwd_kernel<N, M, WT, bf16_t>), dim3(blocks_for(a.nblocks)),
+        hipLaunchKernelGGL((mp_fwd_kernel<N, M, WT, bf16_t>), dim3(noise_blocks_for(a.nblocks)),
                            dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((mp_fwd_kernel<N, M, WT, float>), dim3(blocks_for(a.nblocks)),
+        hipLaunchKernelGGL((mp_fwd_kernel<N, M, WT, float>), dim3(noise_blocks_for(a.nblocks)),
                            dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
@@ -376,7 +397,7 @@ hipError_t bwd_nm(const MpArgs &a, hipStream_t s) {
         hipLaunchKernelGGL((mp_bwd_kernel<N, M, true>), dim3(blocks_for(a.nblocks)),
                            dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((mp_bwd_kernel<N, M, false>), dim3(blocks_for(a.nblocks)),
+        hipLaunchKernelGGL((mp_bwd_kernel<N, M, false>), dim3(noise_blocks_for(a.nblocks)),
                            dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
