@@ -540,8 +540,26 @@ __global__ __launch_bounds__(kThreads) void fwd24_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // Backward to the logits (section 3.2 information flow; section 3.4 Eq. 8):
 //   dm_j = G_j w_j - 2 lambda w_j (w_j m_j),  dy_i = sum_j S_ij dm_j,
-//   dz_i = (kappa/tau) y_i (dy_i - sum_k y_k dy_k)       (fp64 arithmetic)
+//   dz_i = (kappa/tau) y_i (dy_i - sum_k y_k dy_k).
+// With m_j = sum of y_k over the candidates that keep position j and mb_j the
+// sum over those that drop it, dy_i - sum_k y_k dy_k (for sum_k y_k = 1) is
+//   t_i = sum_{j in S_i} mb_j dm_j - sum_{j not in S_i} m_j dm_j,
+// four products of fp32 values whose factors mb_j, m_j are small exactly
+// where dy_i - sum y dy cancels (the dominant candidate: every y_k but its
+// own is small), so t_i is formed in fp32 without that cancellation.
 // ---------------------------------------------------------------------------
+// mb_j: sum of y_i over the candidates that drop position j.
+__device__ __forceinline__ void soft_mask4_complement(const float *y, float *mb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 6; ++i)
+            if (!((C24::mask[i] >> j) & 1u)) s += y[i];
+        mb[j] = s;
+    }
+}
+
 template <int PHASE, typename WT, typename GT, bool SAVED, bool ADAMW>
 __global__ __launch_bounds__(kThreads) void bwd24_kernel(BwdArgs a) {
     __shared__ float4 stage[3 * kThreads];
@@ -552,7 +570,8 @@ __global__ __launch_bounds__(kThreads) void bwd24_kernel(BwdArgs a) {
     }
     const int64_t npairs = (a.g.nblocks + 1) >> 1;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-    const double two_lambda = 2.0 * a.lambda;
+    const float two_lambda = static_cast<float>(2.0 * a.lambda);
+    const float gscale = static_cast<float>(a.nz.grad_scale);
     for (int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads; base < npairs;
          base += stride) {
         const int64_t p = base + threadIdx.x;
@@ -575,37 +594,35 @@ __global__ __launch_bounds__(kThreads) void bwd24_kernel(BwdArgs a) {
             if (a.accumulate) load12(a.dz, p, two, prev);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
+                const float *yh = y + 6 * h;
+                float m[4], mb[4];
+                soft_mask4(yh, m);
+                soft_mask4_complement(yh, mb);
                 // the regulariser term is that of the applied mask (straight-
                 // through under the hard sample); the Jacobian is y's
-                float m[4];
-                applied_mask4(y + 6 * h, hm[h], !SAVED && a.nz.hard_sample, m);
-                double dm[4];
+                float ma[4];
+                applied_mask4(yh, hm[h], !SAVED && a.nz.hard_sample, ma);
+                float pk[4], qd[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const double wj = static_cast<double>(w[4 * h + j]);
-                    const double u = wj * static_cast<double>(m[j]);
-                    dm[j] = static_cast<double>(G[4 * h + j]) * wj - two_lambda * wj * u;
+                    const float wj = w[4 * h + j];
+                    const float u = wj * ma[j];
+                    const float dm = __builtin_fmaf(G[4 * h + j], wj, -(two_lambda * wj) * u);
+                    pk[j] = mb[j] * dm;
+                    qd[j] = m[j] * dm;
                 }
-                // s = sum_k y_k dy_k / sum_k y_k: dividing by the actual sum of
-                // the fp32 soft index keeps dy_i - s free of the fp32 rounding
-                // of y (for the dominant candidate it is a sum over the others)
-                double dy[6], s = 0.0, ysum = 0.0;
 #pragma unroll
                 for (int i = 0; i < 6; ++i) {
-                    double t = 0.0;
+                    // S_i = {lo, hi}, its complement {c0, c1} (compile-time)
+                    int kp[2] = {0, 0}, dp[2] = {0, 0}, nk = 0, nd = 0;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if ((C24::mask[i] >> j) & 1u) t += dm[j];
-                    dy[i] = t;
-                    s += static_cast<double>(y[6 * h + i]) * t;
-                    ysum += static_cast<double>(y[6 * h + i]);
-                }
-                s /= ysum;
-#pragma unroll
-                for (int i = 0; i < 6; ++i) {
-                    double d = a.nz.grad_scale * static_cast<double>(y[6 * h + i]) * (dy[i] - s);
-                    if (a.accumulate) d += static_cast<double>(prev[6 * h + i]);
-                    dz[6 * h + i] = static_cast<float>(d);
+                    for (int j = 0; j < 4; ++j) {
+                        if ((C24::mask[i] >> j) & 1u) kp[nk++] = j;
+                        else dp[nd++] = j;
+                    }
+                    const float t = (pk[kp[0]] + pk[kp[1]]) - (qd[dp[0]] + qd[dp[1]]);
+                    const float sy = gscale * yh[i];
+                    dz[6 * h + i] = a.accumulate ? __builtin_fmaf(sy, t, prev[6 * h + i]) : sy * t;
                 }
             }
         }
