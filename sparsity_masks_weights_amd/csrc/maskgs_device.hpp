@@ -182,7 +182,13 @@ __device__ __forceinline__ float gumbel_lds(uint32_t x, const float4 *tab) {
     const uint32_t k2 = (x >> 8) | 1u;
     const uint32_t v = k2 < (1u << 24) - k2 ? k2 : (1u << 24) - k2;
     const uint32_t f = f32_to_bits(static_cast<float>(v));
-    const uint32_t row = (f >> 18) - (127u << 5) + (k2 >> 23) * (24u * 32u);
+    // side * 768: the top bit of x is bit 23 of k2, spread by an arithmetic
+    // shift (kept as shift and mask: two dual-issue instructions, where a
+    // compare and select would take two single-issue ones)
+    int32_t spread = static_cast<int32_t>(x) >> 31;
+    asm("" : "+v"(spread));
+    const uint32_t side_rows = static_cast<uint32_t>(spread) & (24u * 32u);
+    const uint32_t row = (f >> 18) - (127u << 5) + side_rows;
     const float d = bits_to_f32((f & 0x3FFFFu) | 0x3F800000u) - 1.015625f;
     const float4 c = tab[row];
     return fresh_reg(

@@ -322,12 +322,14 @@ __device__ __forceinline__ void softmax6(const float *a, float *y) {
     float amax = a[0];
 #pragma unroll
     for (int i = 1; i < 6; ++i) amax = fmaxf(amax, a[i]);
-    float s = 0.0f;
+    // exponent (a_i - amax) log2(e) + 64 as one fused multiply-add per
+    // candidate: the rounding of the shared offset scales every exponential
+    // alike and cancels in the normalisation
+    const float off = __builtin_fmaf(-amax, 1.44269504088896341f, 64.0f);
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-        e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(a[i] - amax, 1.44269504088896341f, 64.0f));
-        s += e[i];
-    }
+    for (int i = 0; i < 6; ++i)
+        e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(a[i], 1.44269504088896341f, off));
+    const float s = ((e[0] + e[1]) + (e[2] + e[3])) + (e[4] + e[5]);
     const float inv = __builtin_amdgcn_rcpf(s);
 #pragma unroll
     for (int i = 0; i < 6; ++i) y[i] = e[i] * inv;
@@ -338,9 +340,13 @@ __device__ __forceinline__ void soft_mask4(const float *y, float *m) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         float s = 0.0f;
+        bool first = true;
 #pragma unroll
         for (int i = 0; i < 6; ++i)
-            if ((C24::mask[i] >> j) & 1u) s += y[i];
+            if ((C24::mask[i] >> j) & 1u) {
+                s = first ? y[i] : s + y[i];
+                first = false;
+            }
         m[j] = s;
     }
 }
@@ -437,8 +443,12 @@ __device__ __forceinline__ void pair_noise(const Geometry &g, const Noise &nz, i
 // a_i = fp32(fp32(kappa z_i + g_i) * fp32(1/tau)).
 __device__ __forceinline__ void pair_logits(const Noise &nz, const float (&z)[12],
                                             const float (&g12)[12], float (&a12)[12]) {
+    // kappa and 1/tau in vector registers: an instruction that reads a scalar
+    // register does not dual-issue
+    float kappa = nz.kappa, tau_inv = nz.tau_inv;
+    asm volatile("" : "+v"(kappa), "+v"(tau_inv));
 #pragma unroll
-    for (int i = 0; i < 12; ++i) a12[i] = __builtin_fmaf(nz.kappa, z[i], g12[i]) * nz.tau_inv;
+    for (int i = 0; i < 12; ++i) a12[i] = __builtin_fmaf(kappa, z[i], g12[i]) * tau_inv;
 }
 
 // Soft index of a pair from its logits and noise and, under the hard-sample
@@ -553,9 +563,13 @@ __device__ __forceinline__ void soft_mask4_complement(const float *y, float *mb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         float s = 0.0f;
+        bool first = true;
 #pragma unroll
         for (int i = 0; i < 6; ++i)
-            if (!((C24::mask[i] >> j) & 1u)) s += y[i];
+            if (!((C24::mask[i] >> j) & 1u)) {
+                s = first ? y[i] : s + y[i];
+                first = false;
+            }
         mb[j] = s;
     }
 }

@@ -63,13 +63,16 @@ using C48 = Cands<4, 8>;
 // one 24 KB copy of the noise coefficient table next to each wave's LDS
 // slice, and the grid holds the workgroups that fit the CUs at once (each
 // wave then walks its share of the tiles):
-//  - forward and regulariser (8960 B slice per wave): 4 waves, 2 workgroups
-//    per CU (120.8 KB), the 2 waves per SIMD their 170-240 registers allow;
+//  - forward and regulariser (8960 B slice per wave): 12 waves, one
+//    workgroup per CU (129 KB), 3 waves per SIMD within 168 registers (a few
+//    bytes of pointer spills); against 2 workgroups of 4 waves at up to 240
+//    registers, the forward without a saved soft index took 1.70 instead of
+//    1.86 ms on a 24576x6144 tensor and the one saving it 2.33 instead of 2.36;
 //  - backward recomputing the soft index (17920 B tile per wave): 7 waves,
 //    one workgroup per CU (150 KB); 3 with accumulation (a second tile);
 //  - the sampled diagnostics (17920 B tile): 7 waves, one per CU.
-constexpr int kNoiseWaves = 4;
-constexpr int kNoiseWgPerCU = 2;
+constexpr int kNoiseWaves = 12;
+constexpr int kNoiseWgPerCU = 1;
 constexpr int bwd48_waves(bool saved, bool acc) { return saved ? 1 : (acc ? 3 : 7); }
 constexpr int kStatsNoiseWaves = 7;
 
@@ -289,9 +292,13 @@ __device__ __forceinline__ void philox_call(uint64_t q, uint32_t step, uint32_t 
 // v: logits z on entry, a_i = fp32(fp32(kappa z_i + g_i) * fp32(1/tau)) on exit.
 __device__ __forceinline__ void logits70(float (&v)[kK], uint64_t gb, const Geometry &g,
                                          const Noise &nz, const float4 *gtab) {
+    // kappa and 1/tau in vector registers: an instruction that reads a scalar
+    // register does not dual-issue
+    float kappa = nz.kappa, tau_inv = nz.tau_inv;
+    asm volatile("" : "+v"(kappa), "+v"(tau_inv));
     if (nz.no_noise) {
 #pragma unroll
-        for (int i = 0; i < kK; ++i) v[i] = __builtin_fmaf(nz.kappa, v[i], 0.0f) * nz.tau_inv;
+        for (int i = 0; i < kK; ++i) v[i] = __builtin_fmaf(kappa, v[i], 0.0f) * tau_inv;
         return;
     }
     const uint64_t n0 = gb * static_cast<uint64_t>(kK);
@@ -309,7 +316,7 @@ __device__ __forceinline__ void logits70(float (&v)[kK], uint64_t gb, const Geom
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int i = 4 * c + u;
-            if (i < kK) v[i] = __builtin_fmaf(nz.kappa, v[i], gumbel_lds(wd[u], gtab)) * nz.tau_inv;
+            if (i < kK) v[i] = __builtin_fmaf(kappa, v[i], gumbel_lds(wd[u], gtab)) * tau_inv;
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) prev[u] = cur[u];
@@ -335,10 +342,14 @@ __device__ __forceinline__ void softmax70(float (&v)[kK], uint32_t *hard_mask = 
         }
         amax = fmaxf(amax, v[i]);
     }
+    // exponent (a_i - amax) log2(e) + 64 as one fused multiply-add per
+    // candidate: the rounding of the shared offset scales every exponential
+    // alike and cancels in the normalisation
+    const float off = __builtin_fmaf(-amax, 1.44269504088896341f, 64.0f);
     float s = 0.0f;
 #pragma unroll
     for (int i = 0; i < kK; ++i) {
-        v[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i] - amax, 1.44269504088896341f, 64.0f));
+        v[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i], 1.44269504088896341f, off));
         s += v[i];
     }
     const float inv = __builtin_amdgcn_rcpf(s);
@@ -347,15 +358,76 @@ __device__ __forceinline__ void softmax70(float (&v)[kK], uint32_t *hard_mask = 
     if (SAMPLE) *hard_mask = best;
 }
 
-// Soft mask m_j = sum_i y_i S_ij (Eq. 7), candidates in table order.
-__device__ __forceinline__ void soft_mask8(const float (&y)[kK], float (&m)[8]) {
+// Each candidate's mask splits into a low half (positions 0-3) and a high half
+// (4-7).  kSplit holds both halves of every candidate and marks the first
+// candidate, in table order, with each half, where a sum over the candidates
+// sharing that half starts.  A compile-time table: unrolled uses fold away.
+struct SplitTable {
+    uint8_t lo[kK], hi[kK];
+    bool lo_first[kK], hi_first[kK];
+    constexpr SplitTable() : lo(), hi(), lo_first(), hi_first() {
+        bool seen_lo[16] = {}, seen_hi[16] = {};
+        for (int i = 0; i < kK; ++i) {
+            lo[i] = static_cast<uint8_t>(C48::at(i) & 15u);
+            hi[i] = static_cast<uint8_t>(C48::at(i) >> 4);
+            lo_first[i] = !seen_lo[lo[i]];
+            hi_first[i] = !seen_hi[hi[i]];
+            seen_lo[lo[i]] = true;
+            seen_hi[hi[i]] = true;
+        }
+    }
+};
+constexpr SplitTable kSplit{};
+
+// Sum of H[h] over the half patterns h (0..15) that hold bit j (SET) or lack
+// it (!SET): 8 terms, in ascending h.
+template <bool SET>
+__device__ __forceinline__ float half_sum(const float (&H)[16], int j) {
+    float s = 0.0f;
+    bool first = true;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m[j] = 0.0f;
+    for (int h = 0; h < 16; ++h) {
+        if ((((h >> j) & 1) != 0) == SET) {
+            s = first ? H[h] : s + H[h];
+            first = false;
+        }
+    }
+    return s;
+}
+
+// Soft mask m_j = sum_i y_i S_ij (Eq. 7) and, with COMPL, its complement
+// mb_j = the sum of y_i over the candidates that drop position j (1 - m_j for a
+// soft index that sums to one, without the cancellation of that difference).
+// The candidates are first summed per half pattern: T(A) over those whose low
+// half is A, U(B) over those whose high half is B; then m_j (j < 4) sums T(A)
+// over the A that hold j and mb_j over the others, and U gives j >= 4: 220
+// additions for both instead of 560 term by term.  Src: a register array or
+// an LDS row.
+template <bool COMPL, typename Src>
+__device__ __forceinline__ void soft_masks8(const Src &y, float (&m)[8], float (&mb)[8]) {
+    float T[16] = {}, U[16] = {};
 #pragma unroll
-    for (int i = 0; i < kK; ++i)
+    for (int i = 0; i < kK; ++i) {
+        const float v = y[i];
+        const int A = kSplit.lo[i], B = kSplit.hi[i];
+        T[A] = kSplit.lo_first[i] ? v : T[A] + v;
+        U[B] = kSplit.hi_first[i] ? v : U[B] + v;
+    }
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if ((C48::at(i) >> j) & 1u) m[j] += y[i];
+    for (int j = 0; j < 4; ++j) {
+        m[j] = half_sum<true>(T, j);
+        m[4 + j] = half_sum<true>(U, j);
+        if (COMPL) {
+            mb[j] = half_sum<false>(T, j);
+            mb[4 + j] = half_sum<false>(U, j);
+        }
+    }
+}
+
+template <typename Src>
+__device__ __forceinline__ void soft_mask8(const Src &y, float (&m)[8]) {
+    float unused[8];
+    soft_masks8<false>(y, m, unused);
 }
 
 // Hard mask of a block (section 3.4, Algorithm 1 inference step): the first
@@ -504,49 +576,30 @@ __global__ __launch_bounds__(kWave * kNoiseWaves) void reg48_noise_kernel(RegArg
 // in each pass instead of being kept in registers across passes.
 __device__ __forceinline__ void row_pass_barrier() { asm volatile("" ::: "memory"); }
 
-// Soft mask of a row in fp32 (Eq. 7), candidates in table order.
-__device__ __forceinline__ void row_soft_mask(const float *row, float (&m)[8]) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) m[j] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kK; ++i) {
-        const float y = row[i];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if ((C48::at(i) >> j) & 1u) m[j] += y;
-    }
-}
-
-// Kept positions of every candidate, ascending: kPos.p[i][k] is the k-th set
-// bit of S_i.  A compile-time table, so unrolled uses fold to constants.
+// Kept and dropped positions of every candidate, ascending: kPos.p[i][k] is
+// the k-th set bit of S_i, kPos.c[i][k] the k-th clear one.  A compile-time
+// table, so unrolled uses fold to constants.
 struct PosTable {
-    uint8_t p[kK][4];
-    constexpr PosTable() : p() {
+    uint8_t p[kK][4], c[kK][4];
+    constexpr PosTable() : p(), c() {
         for (int i = 0; i < kK; ++i) {
-            int k = 0;
-            for (int j = 0; j < 8; ++j)
+            int k = 0, n = 0;
+            for (int j = 0; j < 8; ++j) {
                 if ((C48::at(i) >> j) & 1u) p[i][k++] = static_cast<uint8_t>(j);
+                else c[i][n++] = static_cast<uint8_t>(j);
+            }
         }
     }
 };
 constexpr PosTable kPos{};
 
-// Soft mask of a row, summed in fp64 (Eq. 7).
-__device__ __forceinline__ void row_soft_mask_f64(const float *row, double (&md)[8]) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) md[j] = 0.0;
-#pragma unroll
-    for (int i = 0; i < kK; ++i) {
-        const double y = static_cast<double>(row[i]);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) md[kPos.p[i][k]] += y;
-    }
-}
-
-// Backward (section 3.2 information flow; section 3.4 Eq. 8), fp64 arithmetic:
-// dm_j = G_j w_j - 2 lambda w_j (w_j m_j); sum_i y_i dy_i = sum_j m_j dm_j;
-// dz_i = (kappa/tau) y_i (dy_i - s), dy_i = sum_{j in S_i} dm_j, with
-// s = sum_i y_i dy_i / sum_i y_i.
+// Backward (section 3.2 information flow; section 3.4 Eq. 8), fp32:
+// dm_j = G_j w_j - 2 lambda w_j (w_j m_j); dz_i = (kappa/tau) y_i (dy_i - s)
+// with dy_i = sum_{j in S_i} dm_j and s = sum_i y_i dy_i = sum_j m_j dm_j.  For a
+// soft index summing to one, dy_i - s = sum_{j in S_i} mb_j dm_j -
+// sum_{j not in S_i} m_j dm_j (mb_j = 1 - m_j, summed directly): where one
+// candidate dominates, every term of its sum is small, so the difference of
+// two nearly equal numbers that dy_i - s would take in fp32 never arises.
 template <typename WT, typename GT, bool SAVED, bool ACC, bool ADAMW, bool SAMPLE>
 __global__ __launch_bounds__(kWave * bwd48_waves(SAVED, ACC)) void bwd48_kernel(BwdArgs a) {
     constexpr int W = bwd48_waves(SAVED, ACC);
@@ -562,7 +615,8 @@ __global__ __launch_bounds__(kWave * bwd48_waves(SAVED, ACC)) void bwd48_kernel(
     const float *pv = reinterpret_cast<const float *>(prev4[ACC ? wv : 0]);
     const int lane = lane_id();
     const int64_t ntiles = tile_count(a.g.nblocks);
-    const double two_lambda = 2.0 * a.lambda;
+    const float two_lambda = static_cast<float>(2.0 * a.lambda);
+    const float gscale = static_cast<float>(a.nz.grad_scale);
     for (int64_t tile = static_cast<int64_t>(blockIdx.x) * W + wv; tile < ntiles;
          tile += static_cast<int64_t>(gridDim.x) * W) {
         const int64_t b0 = tile * kWave;
@@ -592,51 +646,32 @@ __global__ __launch_bounds__(kWave * bwd48_waves(SAVED, ACC)) void bwd48_kernel(
                 for (int i = 0; i < kK; ++i) row[i] = v[i];
                 row_pass_barrier();
             }
-            float m[8];
-            double md[8], dm[8];
-            row_soft_mask_f64(row, md);
+            float m[8], mb[8];
+            soft_masks8<true>(row, m, mb);
             // the regulariser term is that of the applied mask (straight-through
             // under the hard sample); the Jacobian below is y's
             const bool hard = !SAVED && SAMPLE;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                m[j] = hard ? (((hm >> j) & 1u) ? 1.0f : 0.0f) : static_cast<float>(md[j]);
-            // s = sum_i y_i dy_i / sum_i y_i = sum_j m_j dm_j / (sum_j m_j / 4): the
-            // division by the actual sum of the fp32 soft index keeps dy_i - s
-            // free of the fp32 rounding of y (see the 2:4 backward)
-            double s = 0.0, msum = 0.0;
+            float pk[8], qd[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const double wj = static_cast<double>(w[j]);
-                dm[j] = static_cast<double>(G[j]) * wj - two_lambda * wj * (wj * m[j]);
-                s += md[j] * dm[j];
-                msum += md[j];
+                const float ma = hard ? (((hm >> j) & 1u) ? 1.0f : 0.0f) : m[j];
+                const float u = w[j] * ma;
+                const float dm = __builtin_fmaf(G[j], w[j], -(two_lambda * w[j]) * u);
+                pk[j] = mb[j] * dm;
+                qd[j] = m[j] * dm;
             }
-            s = s * 4.0 / msum;
-            // dy_i = (dm_a + dm_b) + (dm_c + dm_d) for S_i = {a < b < c < d}:
-            // two of the 28 pair sums per candidate
-            double pair[8][8];
-#pragma unroll
-            for (int p = 0; p < 8; ++p)
-#pragma unroll
-                for (int q = p + 1; q < 8; ++q) pair[p][q] = dm[p] + dm[q];
             row_pass_barrier();
             const float *prow = pv + lane * kK;
-            const float scale32 = static_cast<float>(a.nz.grad_scale);
 #pragma unroll
             for (int i = 0; i < kK; ++i) {
-                const int p0 = kPos.p[i][0], p1 = kPos.p[i][1];
-                const int p2 = kPos.p[i][2], p3 = kPos.p[i][3];
-                const double dys = (pair[p0][p1] + pair[p2][p3]) - s;
-                if (ACC) {
-                    const double d = a.nz.grad_scale * static_cast<double>(row[i]) * dys +
-                                     static_cast<double>(prow[i]);
-                    row[i] = static_cast<float>(d);
-                } else {
-                    // the cancellation dy_i - s is taken in fp64; the scaling by
-                    // (kappa/tau) y_i adds three fp32 roundings (< 3e-7 relative)
-                    row[i] = (scale32 * row[i]) * static_cast<float>(dys);
-                }
+                // (pair + pair) sums over S_i and its complement; the pair sums
+                // are shared between candidates
+                const float t = ((pk[kPos.p[i][0]] + pk[kPos.p[i][1]]) +
+                                 (pk[kPos.p[i][2]] + pk[kPos.p[i][3]])) -
+                                ((qd[kPos.c[i][0]] + qd[kPos.c[i][1]]) +
+                                 (qd[kPos.c[i][2]] + qd[kPos.c[i][3]]));
+                const float sy = gscale * row[i];
+                row[i] = ACC ? __builtin_fmaf(sy, t, prow[i]) : sy * t;
             }
         }
         wave_sync();
@@ -667,7 +702,7 @@ __global__ __launch_bounds__(kWave) void reg48_saved_kernel(RegArgs a) {
         __syncthreads();
         if (lane < nb) {
             float m[8], w[8];
-            row_soft_mask(tl + lane * kK, m);
+            soft_mask8(tl + lane * kK, m);
             Io8<WT>::load(a.w, b0 + lane, w);
             float racc = 0.0f;
 #pragma unroll
