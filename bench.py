@@ -5,12 +5,12 @@ LLaMA-2-7B-shaped model (224 tensors, 1.62e9 2:4 blocks, inputs resident in
 HBM): the Gumbel soft-mask forward of every tensor (W (.) M~ in bf16,
 regulariser reduced) with the hard mask of the same logits (argmax, bit
 packing, 2:4 values and 2-bit indices) produced in the same pass, then the
-logit backward of every tensor.  With --step auto (the default) the 2:4
-forward saves nothing and the backward draws the soft index again from z,
-while the 4:8 forward saves the soft index for the backward: the faster design
-of each pattern on this chip.  --step recompute|saved forces one; the other
-design is timed too (`other_step`), and so is the unfused order (forward,
-backward, separate extraction).  Prior seeding, an initialisation step, is
+logit backward of every tensor.  By default (--step recompute) the forward
+saves nothing and the backward draws the soft index again from z, the faster
+design for both patterns on this chip; --step saved has the forward write the
+soft index and the backward read it.  The other design is timed too
+(`other_step`), and so is the unfused order (forward, backward, separate
+extraction).  Prior seeding, an initialisation step, is
 timed once after the steps.  Then the training step with the logit update
 fused into the backward (maskgs_bwd_adamw) is timed with the soft index saved
 and recomputed (`train_step`, --no-train-step skips it), one pass of the
@@ -62,6 +62,11 @@ KERNEL_SOURCES = ["sparsity_masks_weights_amd/csrc/maskgs_k24.hip",
                   "sparsity_masks_weights_amd/csrc/maskgs_device.hpp",
                   "sparsity_masks_weights_amd/csrc/maskgs_gumbel_table.inc"]
 
+# kernel kinds a --profile run can launch (the two hs_ kinds: the step's
+# kernels under the hard Gumbel-max sample)
+PROFILE_KINDS = ("fwd", "fwd_hard", "fwd_hard_noy", "bwd", "bwd_rc", "hard", "hs_fwd_hard_noy",
+                 "hs_bwd_rc")
+
 # what each kernel kind is, in entry-point terms
 KIND_DESC = {
     "fwd": "maskgs_fwd (soft index saved)",
@@ -79,10 +84,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama7b_all_linear")
-    ap.add_argument("--step", choices=("auto", "recompute", "saved"), default="auto",
+    ap.add_argument("--step", choices=("recompute", "saved"), default="recompute",
                     help="recompute: the backward draws the soft index again from z; saved: the "
-                         "forward writes it and the backward reads it; auto: recompute for 2:4, "
-                         "saved for 4:8")
+                         "forward writes it and the backward reads it")
     ap.add_argument("--streams", type=int, default=2,
                     help="worker streams the launches of a phase alternate between (1: in order)")
     ap.add_argument("--layers", type=int, default=None,
@@ -94,8 +98,10 @@ def parse():
                     help="time the step and the other step design only")
     ap.add_argument("--no-sub", action="store_true",
                     help="skip the q_proj, MLP-anneal and 4:8 sub-results")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--profile", default=None, metavar="KINDS",
+                    help="counter runs: launch each listed kernel kind (comma-separated: "
+                         + ", ".join(PROFILE_KINDS) + ") 3 times on the workload's largest "
+                         "tensor, in order, print their launch times and exit")
     args = ap.parse_args()
     if args.streams < 1:
         ap.error("--streams must be at least 1")
@@ -113,9 +119,7 @@ def source_hash() -> str:
 
 
 def step_mode(args, wl) -> str:
-    if args.step != "auto":
-        return args.step
-    return "recompute" if (wl.n, wl.m) == (2, 4) else "saved"
+    return args.step
 
 
 def step_kinds(mode):
@@ -850,6 +854,35 @@ def cpu_baseline_linear(wl, bufs, mp_bufs, min_secs=8.0):
                       f"masked weights + policy gradient, {secs:.1f} s of CPU time"}
 
 
+def run_profile(mg, wl, args, dev):
+    """Each listed kind launched 3 times on the workload's largest tensor, on
+    the main stream, one after another (the dispatch order a counter run
+    sees); prints the launch times as one JSON line."""
+    kinds = [k for k in args.profile.split(",") if k]
+    bad = [k for k in kinds if k not in PROFILE_KINDS]
+    if bad:
+        raise SystemExit(f"--profile: unknown kind(s) {bad}; known: {', '.join(PROFILE_KINDS)}")
+    big = max(wl.tensors, key=lambda t: t.rows * t.cols)
+    sess = Session(mg, wl, [big], args, dev, with_y=True)
+    hs = mg.SampleParams(0, 0, wl.kappa, wl.tau, mg.MASKGS_HARD_SAMPLE)
+    d = sess.bufs[0]
+    times = {}
+    for kind in kinds:
+        base, pref = kind, None
+        if kind.startswith("hs_"):
+            base, pref = kind[3:], ctypes.byref(hs)
+        for _ in range(3):
+            e0, e1 = sess.ev(), sess.ev()
+            e0.record(sess.stream)
+            sess.call(base, d, sess.sptr, pref)
+            e1.record(sess.stream)
+            sess.torch.cuda.synchronize()
+            times.setdefault(kind, []).append(round(e0.elapsed_time(e1) * 1e3, 2))
+    print(json.dumps({"profile": times, "unit": "us per launch", "workload": wl.key,
+                      "tensor": f"{big.name} {big.rows}x{big.cols}", "blocks": d["B"],
+                      "source_hash": source_hash()}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -869,16 +902,13 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     wl = WORKLOADS[args.workload]
+    if args.profile:
+        run_profile(mg, wl, args, dev)
+        return
     specs = wl.tensors
     if args.layers is not None:
         specs = [t for t in specs if t.tensor_id < 7 * args.layers]
     result, sess = run_main(mg, wl, specs, args, dev, extras=not args.no_extras)
-    if args.calibrate_copy:
-        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
     del sess
     gc.collect()
     torch.cuda.empty_cache()

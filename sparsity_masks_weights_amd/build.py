@@ -56,5 +56,21 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+PROBE_SRC = os.path.join(PKG, "calib", "roofline_probe.hip")
+PROBE = os.path.join(PKG, "calib", "roofline_probe")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile the roofline calibration program (calib/roofline_probe): HBM
+    streams and VALU loops of known size, run on its own and under rocprofv3."""
+    cmd = [hipcc(), *[f for f in HIPCC_FLAGS if f != "-fPIC"], PROBE_SRC, "-o", PROBE + ".tmp"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(PROBE + ".tmp", PROBE)
+    return PROBE
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_probe(verbose=True))

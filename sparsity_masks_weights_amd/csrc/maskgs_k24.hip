@@ -454,15 +454,18 @@ __device__ __forceinline__ void pair_logits(const Noise &nz, const float (&z)[12
 // Soft index of a pair from its logits and noise and, under the hard-sample
 // flag, the masks of its two Gumbel-max samples S[first argmax a] (0
 // otherwise).
+// need_y false skips the soft index under the hard sample (a forward that
+// applies the sample and saves no soft index has no use for it).
 __device__ __forceinline__ void pair_sample(const Noise &nz, const float (&z)[12],
                                             const float (&g12)[12], float (&y)[12],
-                                            uint32_t (&hm)[2]) {
+                                            uint32_t (&hm)[2], bool need_y = true) {
     float a12[12];
     pair_logits(nz, z, g12, a12);
     hm[0] = hm[1] = 0u;
     if (nz.hard_sample) {
         hm[0] = cand_mask6(first_argmax6(a12));
         hm[1] = cand_mask6(first_argmax6(a12 + 6));
+        if (!need_y) return;
     }
     softmax6(a12, y);
     softmax6(a12 + 6, y + 6);
@@ -526,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void fwd24_kernel(FwdArgs a) {
                 hard_pair<WT>(a.idx, a.bits, a.values, a.val_idx, p, two, z, wd);
             }
             uint32_t hm[2];
-            pair_sample(a.nz, z, g12, y, hm);
+            pair_sample(a.nz, z, g12, y, hm, YSAVE);
             float racc = 0.0f;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -690,7 +693,8 @@ __global__ __launch_bounds__(kThreads) void reg24_kernel(RegArgs a) {
             float z[12], g12[12];
             load12(a.z, p, two, z);
             pair_noise<PHASE>(a.g, a.nz, p, gtab, g12);
-            pair_sample(a.nz, z, g12, y, hm);
+            // the regulariser of a hard sample needs only its mask
+            pair_sample(a.nz, z, g12, y, hm, false);
         }
         float racc = 0.0f;
 #pragma unroll

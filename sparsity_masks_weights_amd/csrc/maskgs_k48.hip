@@ -511,7 +511,13 @@ __global__ __launch_bounds__(kWave * kNoiseWaves) void fwd48_kernel(FwdArgs a) {
             }
             logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz, gtab);
             uint32_t hm = 0u;
-            softmax70<SAMPLE>(v, &hm);
+            if (SAMPLE && !a.y) {
+                // the forward applies the sample and saves no soft index:
+                // only the sample's candidate is needed
+                hm = argmax_key70(v) & 0xFFu;
+            } else {
+                softmax70<SAMPLE>(v, &hm);
+            }
             float m[8], w[8], out[8];
             applied_mask8(v, hm, SAMPLE, m);
             Io8<WT>::load(a.w, b, w);
@@ -553,7 +559,12 @@ __global__ __launch_bounds__(kWave * kNoiseWaves) void reg48_noise_kernel(RegArg
         if (lane < nb) {
             logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz, gtab);
             uint32_t hm = 0u;
-            softmax70<SAMPLE>(v, &hm);
+            if (SAMPLE) {
+                // the regulariser of the hard sample needs only its candidate
+                hm = argmax_key70(v) & 0xFFu;
+            } else {
+                softmax70<false>(v, &hm);
+            }
             float m[8], w[8];
             applied_mask8(v, hm, SAMPLE, m);
             Io8<WT>::load(a.w, b, w);
