@@ -484,7 +484,10 @@ __device__ __forceinline__ int64_t tile_count(int64_t nblocks) {
 // ---------------------------------------------------------------------------
 // Forward (noise kernel, registers).
 // ---------------------------------------------------------------------------
-template <typename WT, typename OT, bool HARD, bool SAMPLE>
+// YOUT: the soft index is saved (a.y); without it, a forward that applies the
+// hard sample computes only the sample's candidate.  A compile-time switch, so
+// that the register allocation of each variant sees only its own path.
+template <typename WT, typename OT, bool HARD, bool SAMPLE, bool YOUT>
 __global__ __launch_bounds__(kWave * kNoiseWaves) void fwd48_kernel(FwdArgs a) {
     __shared__ float4 stage4[kNoiseWaves][kHalf * kK / 4];
     __shared__ float4 gtab[kGumbelRows];
@@ -511,7 +514,7 @@ __global__ __launch_bounds__(kWave * kNoiseWaves) void fwd48_kernel(FwdArgs a) {
             }
             logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz, gtab);
             uint32_t hm = 0u;
-            if (SAMPLE && !a.y) {
+            if constexpr (SAMPLE && !YOUT) {
                 // the forward applies the sample and saves no soft index:
                 // only the sample's candidate is needed
                 hm = argmax_key70(v) & 0xFFu;
@@ -530,7 +533,7 @@ __global__ __launch_bounds__(kWave * kNoiseWaves) void fwd48_kernel(FwdArgs a) {
             reg += static_cast<double>(racc);
             Io8<OT>::store(a.out, b, out);
         }
-        if (a.y) tile_out(a.y, b0, nb, stage, v);
+        if (YOUT) tile_out(a.y, b0, nb, stage, v);
     }
     if (a.reg) reduce_add_wave(reg, a.reg);
 }
@@ -967,26 +970,33 @@ hipError_t go_waves(Kern kernel, const A &args, int64_t nblocks, int waves, int 
 
 }  // namespace
 
-template <bool HARD, bool SAMPLE>
+template <bool HARD, bool SAMPLE, bool YOUT>
 hipError_t fwd48_dispatch(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype out_dt, hipStream_t s) {
     const int64_t n = a.g.nblocks;
     const int w = kNoiseWaves, c = kNoiseWgPerCU;
     if (w_dt == MASKGS_BF16 && out_dt == MASKGS_BF16)
-        return go_waves(fwd48_kernel<bf16_t, bf16_t, HARD, SAMPLE>, a, n, w, c, s);
+        return go_waves(fwd48_kernel<bf16_t, bf16_t, HARD, SAMPLE, YOUT>, a, n, w, c, s);
     if (w_dt == MASKGS_BF16)
-        return go_waves(fwd48_kernel<bf16_t, float, HARD, SAMPLE>, a, n, w, c, s);
+        return go_waves(fwd48_kernel<bf16_t, float, HARD, SAMPLE, YOUT>, a, n, w, c, s);
     if (out_dt == MASKGS_BF16)
-        return go_waves(fwd48_kernel<float, bf16_t, HARD, SAMPLE>, a, n, w, c, s);
-    return go_waves(fwd48_kernel<float, float, HARD, SAMPLE>, a, n, w, c, s);
+        return go_waves(fwd48_kernel<float, bf16_t, HARD, SAMPLE, YOUT>, a, n, w, c, s);
+    return go_waves(fwd48_kernel<float, float, HARD, SAMPLE, YOUT>, a, n, w, c, s);
+}
+
+template <bool HARD, bool SAMPLE>
+hipError_t fwd48_dispatch_y(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype out_dt,
+                            hipStream_t s) {
+    return a.y ? fwd48_dispatch<HARD, SAMPLE, true>(a, w_dt, out_dt, s)
+               : fwd48_dispatch<HARD, SAMPLE, false>(a, w_dt, out_dt, s);
 }
 
 hipError_t launch_fwd48(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype out_dt, hipStream_t s) {
     const bool hard = a.idx || a.bits;
     if (a.nz.hard_sample)
-        return hard ? fwd48_dispatch<true, true>(a, w_dt, out_dt, s)
-                    : fwd48_dispatch<false, true>(a, w_dt, out_dt, s);
-    return hard ? fwd48_dispatch<true, false>(a, w_dt, out_dt, s)
-                : fwd48_dispatch<false, false>(a, w_dt, out_dt, s);
+        return hard ? fwd48_dispatch_y<true, true>(a, w_dt, out_dt, s)
+                    : fwd48_dispatch_y<false, true>(a, w_dt, out_dt, s);
+    return hard ? fwd48_dispatch_y<true, false>(a, w_dt, out_dt, s)
+                : fwd48_dispatch_y<false, false>(a, w_dt, out_dt, s);
 }
 
 template <bool SAVED, bool ACC, bool ADAMW, bool SAMPLE>

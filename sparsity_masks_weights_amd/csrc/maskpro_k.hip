@@ -266,11 +266,15 @@ __device__ __forceinline__ void mp_bwd_block(const MpArgs &a, int64_t b, const f
         float mx = q[0];
 #pragma unroll
         for (int l = 1; l < M; ++l) mx = __builtin_fmaxf(mx, q[l]);
+        // e_l = 2^((q_l - mx) log2 e) as one fused multiply-add per position:
+        // the rounding of the shared offset scales every e_l alike and cancels
+        // in e_l / Z
+        const float off = -mx * 1.44269504088896341f;
         float e[M];
         float z = 0.0f;
 #pragma unroll
         for (int l = 0; l < M; ++l) {
-            e[l] = __expf(q[l] - mx);
+            e[l] = __builtin_amdgcn_exp2f(__builtin_fmaf(q[l], 1.44269504088896341f, off));
             z += e[l];
         }
         const float inv = __builtin_amdgcn_rcpf(z);
