@@ -393,16 +393,25 @@ class Session:
 
 
 def recorded(path, workload, kind, blocks, field):
-    """A per-launch counter value recorded (rocprofv3) for `kind` on the
-    workload's largest tensor, used only while the kernel sources hash to the
-    value they were recorded on."""
+    """A per-launch counter value recorded (rocprofv3) for `kind` on a tensor
+    of `blocks` blocks: the workload's own record, else another workload's
+    record of the same N:M pattern and tensor size (the same kernel over the
+    same bytes); used only while the kernel sources hash to the value it was
+    recorded on."""
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        tr = json.load(f).get("workloads", {}).get(workload, {})
-    k = tr.get("kernels", {}).get(kind)
-    if k and tr.get("source_hash") == source_hash() and tr.get("blocks_per_launch") == blocks:
-        return k.get(field)
+        recs = json.load(f).get("workloads", {})
+    from workloads import WORKLOADS
+    nm = f"{WORKLOADS[workload].n}:{WORKLOADS[workload].m}"
+    order = [workload] + [w for w in recs if w != workload]
+    for w in order:
+        tr = recs.get(w, {})
+        if w != workload and tr.get("n_m") != nm:
+            continue
+        k = tr.get("kernels", {}).get(kind)
+        if k and tr.get("source_hash") == source_hash() and tr.get("blocks_per_launch") == blocks:
+            return k.get(field)
     return None
 
 
@@ -455,9 +464,10 @@ def run_main(mg, wl, specs, args, dev, extras=True, cpu_secs=10.0):
     mode = step_mode(args, wl)
     kinds = step_kinds(mode)
     sess = Session(mg, wl, specs, args, dev, with_y=True)
-    # the dominant kernel is chosen from untimed-launch steps, then one of its
-    # launches on a largest tensor is timed alone in each timed step
-    sess.timed_steps(kinds, max(1, args.warmup), 0)
+    # the dominant kernel is chosen from one step after the warm-up steps (the
+    # first launches of a kernel run slower), then one of its launches on a
+    # largest tensor is timed alone in each timed step
+    sess.timed_steps(kinds, 1, max(1, args.warmup))
     dom = sess.dominant(kinds)
     ms_step = sess.timed_steps(kinds, args.steps, 0, timed_kind=dom)
     result = line(sess, ms_step, kinds, args.steps, args, mode)
@@ -691,7 +701,7 @@ def run_qproj_prior(mg, args, dev):
     e1.record(sess.stream)
     torch.cuda.synchronize()
     copy_traffic = sum(sess.bpb[k] for k in kinds) * sess.blocks
-    sess.timed_steps(kinds, max(1, args.warmup), 0)
+    sess.timed_steps(kinds, 1, max(1, args.warmup))
     dom = sess.dominant(kinds)
     nsteps = copies * max(1, args.steps // copies)
     ms = sess.timed_steps(kinds, nsteps, 0, timed_kind=dom)
@@ -704,7 +714,7 @@ def run_qproj_prior(mg, args, dev):
     res["roofline"] = sess.roofline(dom)
     res["prior_init"] = {"ms_per_tensor": round(e0.elapsed_time(e1) / copies, 4)}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, sess.bufs[:1], min_secs=3.0)
+        res["cpu_baseline"] = cpu_baseline(wl, sess.bufs[:1], min_secs=5.0)
     return res
 
 
@@ -723,7 +733,7 @@ def run_mlp_anneal(mg, args, dev):
         sess.params.step = s % wl.steps
         sess.params.kappa = k
         sess.params.tau = t
-    sess.timed_steps(kinds, max(1, args.warmup), 0, schedule=sched)
+    sess.timed_steps(kinds, 1, max(1, args.warmup), schedule=sched)
     dom = sess.dominant(kinds)
     nsteps = wl.steps * max(1, args.steps // wl.steps)
     ms = sess.timed_steps(kinds, nsteps, 0, timed_kind=dom, schedule=sched)
@@ -734,7 +744,7 @@ def run_mlp_anneal(mg, args, dev):
     res["kernels"] = sess.kernel_stats(kinds, nsteps)
     res["roofline"] = sess.roofline(dom)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, sess.bufs[:1], min_secs=3.0)
+        res["cpu_baseline"] = cpu_baseline(wl, sess.bufs, min_secs=5.0)
     return res
 
 
@@ -742,7 +752,7 @@ def run_layer_48(mg, args, dev):
     """Nemotron-4-15B-shaped 4:8 layer set: the step and the other design."""
     from workloads import WORKLOADS
     wl = WORKLOADS["nemotron15b_layer_48"]
-    res, sess = run_main(mg, wl, wl.tensors, args, dev, extras=False, cpu_secs=3.0)
+    res, sess = run_main(mg, wl, wl.tensors, args, dev, extras=False, cpu_secs=5.0)
     del sess
     return res
 
@@ -790,7 +800,9 @@ def host_array(t, shape=None):
 
 def cpu_baseline(wl, bufs, min_secs=10.0):
     """The CPU oracle (all host threads) on whole tensors of the workload, in
-    order, until at least `min_secs` of CPU work: fwd + bwd + hard extract."""
+    order (starting over after the last one), until at least `min_secs` of
+    CPU work: fwd + bwd + hard extract."""
+    import itertools
     import numpy as np
     import torch
     import oracle
@@ -798,7 +810,7 @@ def cpu_baseline(wl, bufs, min_secs=10.0):
     oracle.set_threads(oracle_threads())
     used = oracle.get_threads()
     blocks, secs, tensors = 0, 0.0, 0
-    for d in bufs:
+    for d in itertools.cycle(bufs):
         if tensors and secs >= min_secs:
             break
         spec = d["spec"]
@@ -818,10 +830,12 @@ def cpu_baseline(wl, bufs, min_secs=10.0):
         blocks += d["B"]
         tensors += 1
         del wf, w_raw, zf, gf
+    what = (f"first {tensors} tensor(s) of the same workload" if tensors <= len(bufs) else
+            f"{tensors} tensor passes over the first {len(bufs)} tensor(s) of the workload")
     return {"value": round(blocks / secs, 1), "unit": "weight-blocks/s", "cores": used,
             "kind": "oracle", "host": host_cpu(),
-            "sample": f"first {tensors} tensor(s) of the same workload ({blocks} blocks): fwd + "
-                      f"bwd + hard extract, {secs:.1f} s of CPU time"}
+            "sample": f"{what} ({blocks} blocks): fwd + bwd + hard extract, {secs:.1f} s of "
+                      f"CPU time"}
 
 
 def cpu_baseline_linear(wl, bufs, mp_bufs, min_secs=8.0):
