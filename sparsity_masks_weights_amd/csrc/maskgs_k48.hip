@@ -68,8 +68,11 @@ using C48 = Cands<4, 8>;
 //    bytes of pointer spills); against 2 workgroups of 4 waves at up to 240
 //    registers, the forward without a saved soft index took 1.70 instead of
 //    1.86 ms on a 24576x6144 tensor and the one saving it 2.33 instead of 2.36;
-//  - backward recomputing the soft index (17920 B tile per wave): 7 waves,
-//    one workgroup per CU (150 KB); 3 with accumulation (a second tile);
+//  - backward recomputing the soft index: without accumulation the
+//    register-resident form, 12 waves like the forward (2.54 -> 2.33 ms on
+//    a 24576x6144 tensor against the whole-tile form); with accumulation or
+//    the fused AdamW update the whole-tile form (17920 B tile per wave): 7
+//    waves, one workgroup per CU (150 KB), 3 with accumulation (a second tile);
 //  - the sampled diagnostics (17920 B tile): 7 waves, one per CU.
 constexpr int kNoiseWaves = 12;
 constexpr int kNoiseWgPerCU = 1;
@@ -700,6 +703,99 @@ __global__ __launch_bounds__(kWave * bwd48_waves(SAVED, ACC)) void bwd48_kernel(
     }
 }
 
+// 8 elements of one block from their raw 16-byte words (bf16: one word of
+// pairs; fp32: two words).
+template <typename T>
+__device__ __forceinline__ void unpack8(uint4 r, uint4 r2, float (&v)[8]) {
+    if constexpr (sizeof(T) == 2) {
+        const uint32_t d[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(d[i] << 16);
+            v[2 * i + 1] = __uint_as_float(d[i] & 0xFFFF0000u);
+        }
+    } else {
+        const uint32_t d[8] = {r.x, r.y, r.z, r.w, r2.x, r2.y, r2.z, r2.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(d[i]);
+    }
+}
+
+// Raw 16-byte words of one block's 8 elements (r2 only for fp32).
+template <typename T>
+__device__ __forceinline__ void load8_raw(const void *base, int64_t b, uint4 &r, uint4 &r2) {
+    if constexpr (sizeof(T) == 2) {
+        r = reinterpret_cast<const uint4 *>(base)[b];
+    } else {
+        r = reinterpret_cast<const uint4 *>(base)[2 * b];
+        r2 = reinterpret_cast<const uint4 *>(base)[2 * b + 1];
+    }
+}
+
+// Backward drawing the soft index again (section 3.2 information flow;
+// section 3.4 Eq. 8), register-resident: a block's 70 values stay in
+// registers from the logits to dz, the z tile comes in and the dz tile goes
+// out through the wave's half-tile stage as in the forward, so that 12 waves
+// per CU (3 per SIMD) share one table copy; the bwd48_kernel form keeps the
+// rows in a whole LDS tile and fits 7.  The arithmetic is bwd48_kernel's.  The
+// weights and upstream gradient are requested after the softmax, which keeps
+// them out of the registers the noise needs (requested with the tile they
+// forced 44 bytes of spills per lane).
+template <typename WT, typename GT, bool SAMPLE>
+__global__ __launch_bounds__(kWave * kNoiseWaves) void bwd48_reg_kernel(BwdArgs a) {
+    __shared__ float4 stage4[kNoiseWaves][kHalf * kK / 4];
+    __shared__ float4 gtab[kGumbelRows];
+    load_gumbel_table<kWave * kNoiseWaves>(gtab);
+    __syncthreads();
+    const int wv = threadIdx.x / kWave;
+    float *stage = reinterpret_cast<float *>(stage4[wv]);
+    const int lane = lane_id();
+    const int64_t ntiles = tile_count(a.g.nblocks);
+    const float two_lambda = static_cast<float>(2.0 * a.lambda);
+    const float gscale = static_cast<float>(a.nz.grad_scale);
+    for (int64_t tile = static_cast<int64_t>(blockIdx.x) * kNoiseWaves + wv; tile < ntiles;
+         tile += static_cast<int64_t>(gridDim.x) * kNoiseWaves) {
+        const int64_t b0 = tile * kWave;
+        const int nb = static_cast<int>(a.g.nblocks - b0 < kWave ? a.g.nblocks - b0 : kWave);
+        const int64_t b = b0 + lane;
+        float v[kK];
+        tile_in<false>(a.z, b0, nb, stage, v);
+        if (lane < nb) {
+            logits70(v, a.g.block_offset + static_cast<uint64_t>(b), a.g, a.nz, gtab);
+            uint32_t hm = 0u;
+            softmax70<SAMPLE>(v, &hm);
+            uint4 wr = make_uint4(0u, 0u, 0u, 0u), wr2 = wr, gr = wr, gr2 = wr;
+            load8_raw<WT>(a.w, b, wr, wr2);
+            load8_raw<GT>(a.dout, b, gr, gr2);
+            float m[8], mb[8];
+            soft_masks8<true>(v, m, mb);
+            float w[8], G[8];
+            unpack8<WT>(wr, wr2, w);
+            unpack8<GT>(gr, gr2, G);
+            // the regulariser term is that of the applied mask (straight-through
+            // under the hard sample); the Jacobian is y's
+            float pk[8], qd[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float ma = SAMPLE ? (((hm >> j) & 1u) ? 1.0f : 0.0f) : m[j];
+                const float u = w[j] * ma;
+                const float dm = __builtin_fmaf(G[j], w[j], -(two_lambda * w[j]) * u);
+                pk[j] = mb[j] * dm;
+                qd[j] = m[j] * dm;
+            }
+#pragma unroll
+            for (int i = 0; i < kK; ++i) {
+                const float t = ((pk[kPos.p[i][0]] + pk[kPos.p[i][1]]) +
+                                 (pk[kPos.p[i][2]] + pk[kPos.p[i][3]])) -
+                                ((qd[kPos.c[i][0]] + qd[kPos.c[i][1]]) +
+                                 (qd[kPos.c[i][2]] + qd[kPos.c[i][3]]));
+                v[i] = (gscale * v[i]) * t;
+            }
+        }
+        tile_out(a.dz, b0, nb, stage, v);
+    }
+}
+
 // Regulariser value from a saved soft index.
 template <typename WT>
 __global__ __launch_bounds__(kWave) void reg48_saved_kernel(RegArgs a) {
@@ -1014,6 +1110,20 @@ hipError_t bwd48_dispatch(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt
     return go_waves(bwd48_kernel<float, float, SAVED, ACC, ADAMW, SAMPLE>, a, n, w, c, s);
 }
 
+// The recomputing backward without accumulation: register-resident, 12-wave
+// workgroups, one per CU.
+template <bool SAMPLE>
+hipError_t bwd48_reg_dispatch(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt,
+                              hipStream_t s) {
+    const int64_t n = a.g.nblocks;
+    const int w = kNoiseWaves, c = kNoiseWgPerCU;
+    const bool wb = w_dt == MASKGS_BF16, gb = g_dt == MASKGS_BF16;
+    if (wb && gb) return go_waves(bwd48_reg_kernel<bf16_t, bf16_t, SAMPLE>, a, n, w, c, s);
+    if (wb) return go_waves(bwd48_reg_kernel<bf16_t, float, SAMPLE>, a, n, w, c, s);
+    if (gb) return go_waves(bwd48_reg_kernel<float, bf16_t, SAMPLE>, a, n, w, c, s);
+    return go_waves(bwd48_reg_kernel<float, float, SAMPLE>, a, n, w, c, s);
+}
+
 hipError_t launch_bwd48(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, hipStream_t s) {
     // the hard sample comes with a recomputed soft index only (checked by the API)
     const bool smp = a.nz.hard_sample && !a.y;
@@ -1024,11 +1134,11 @@ hipError_t launch_bwd48(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, 
     }
     if (a.y) return a.accumulate ? bwd48_dispatch<true, true, false, false>(a, w_dt, g_dt, s)
                                  : bwd48_dispatch<true, false, false, false>(a, w_dt, g_dt, s);
-    if (smp)
-        return a.accumulate ? bwd48_dispatch<false, true, false, true>(a, w_dt, g_dt, s)
-                            : bwd48_dispatch<false, false, false, true>(a, w_dt, g_dt, s);
-    return a.accumulate ? bwd48_dispatch<false, true, false, false>(a, w_dt, g_dt, s)
-                        : bwd48_dispatch<false, false, false, false>(a, w_dt, g_dt, s);
+    if (a.accumulate)
+        return smp ? bwd48_dispatch<false, true, false, true>(a, w_dt, g_dt, s)
+                   : bwd48_dispatch<false, true, false, false>(a, w_dt, g_dt, s);
+    return smp ? bwd48_reg_dispatch<true>(a, w_dt, g_dt, s)
+               : bwd48_reg_dispatch<false>(a, w_dt, g_dt, s);
 }
 
 hipError_t launch_reg48(const RegArgs &a, maskgs_dtype w_dt, hipStream_t s) {
