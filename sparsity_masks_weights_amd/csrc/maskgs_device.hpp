@@ -175,22 +175,26 @@ __device__ __forceinline__ float fresh_reg(float x) {
     return r;
 }
 
-// g of the contract for Philox word x.  The row index is side * 768 + b * 32
-// + q, read off the exponent and the top 5 mantissa bits of fp32(v) (exact);
-// the low 18 mantissa bits give d = v / 2^b - 1 - (q + 1/2)/32, also exact.
+// g of the contract for Philox word x.  With spread = x >> 31 (arithmetic:
+// all ones on side 1), v = min(k2, 2^24 - k2) is ((x ^ spread) >> 8) | 1: on
+// side 1 the complemented word gives 2^24 - k2 (for k2 = (x >> 8) | 1, the
+// complement's (~x >> 8) | 1 is 2^24 - k2 whatever the parity of x >> 8).
+// The row is side * 768 + b * 32 + q, read off the exponent and the top 5
+// mantissa bits of fp32(v) (exact), and addressed in bytes: (f >> 14) masked
+// is 16 (127 * 32 + b * 32 + q); the low 18 mantissa bits give
+// d = v / 2^b - 1 - (q + 1/2)/32, also exact.
 __device__ __forceinline__ float gumbel_lds(uint32_t x, const float4 *tab) {
-    const uint32_t k2 = (x >> 8) | 1u;
-    const uint32_t v = k2 < (1u << 24) - k2 ? k2 : (1u << 24) - k2;
-    const uint32_t f = f32_to_bits(static_cast<float>(v));
-    // side * 768: the top bit of x is bit 23 of k2, spread by an arithmetic
-    // shift (kept as shift and mask: two dual-issue instructions, where a
-    // compare and select would take two single-issue ones)
+    // shift and mask (dual-issue instructions) rather than a compare and a
+    // select for the side; kept from being turned into one by the compiler
     int32_t spread = static_cast<int32_t>(x) >> 31;
     asm("" : "+v"(spread));
-    const uint32_t side_rows = static_cast<uint32_t>(spread) & (24u * 32u);
-    const uint32_t row = (f >> 18) - (127u << 5) + side_rows;
+    const uint32_t v = ((x ^ static_cast<uint32_t>(spread)) >> 8) | 1u;
+    const uint32_t f = f32_to_bits(static_cast<float>(v));
+    const uint32_t side_bytes = static_cast<uint32_t>(spread) & (24u * 32u * 16u);
+    const uint32_t off = ((f >> 14) & 0x1FFF0u) + side_bytes;
     const float d = bits_to_f32((f & 0x3FFFFu) | 0x3F800000u) - 1.015625f;
-    const float4 c = tab[row];
+    const float4 c = *reinterpret_cast<const float4 *>(
+        reinterpret_cast<const char *>(tab) + off - (127u << 5) * 16u);
     return fresh_reg(
         __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(c.w, d, c.z), d, c.y), d, c.x));
 }
