@@ -4,7 +4,8 @@ A 4:8 tensor of 16384 x 16384 weights has 33.5M blocks and 2.35G logits (9.4
 GB); a 2:4 tensor of 32768 x 45056 weights has 369M blocks and 2.21G logits.
 Every index and byte offset past 2^31 must be carried in 64 bits: the
 forward with the hard mask fused in and the backward run on the whole tensor
-in the benchmark's launch configuration, and the oracle checks the first,
+in the benchmark's launch configuration (with the soft index saved, and
+recomputed as the benchmark's step does), and the oracle checks the first,
 middle and last rows (noise keyed on their global block indices), the hard
 mask of those rows, and the backward; likewise the linear-space draw and
 policy gradient on [B, M] logits past 2^31 floats.  At most 36 GB of device
@@ -52,29 +53,36 @@ def test_logit_arrays_past_2_31(mg, orc, case):
     y = torch.empty_like(z)
     idx = torch.empty(B, dtype=torch.uint8, device=dev)
     bits = torch.empty((B * m + 7) // 8, dtype=torch.uint8, device=dev)
-    mg.maskgs_fwd_hard(t, p, w, z, out, y, None, idx, bits)
     dz = torch.empty_like(z)
-    mg.maskgs_bwd(t, p, w, None, y, G, lam, dz)
-    torch.cuda.synchronize()
-
-    for r in (0, 1, rows // 2, rows - 2, rows - 1):
-        b0, b1 = r * bpr, (r + 1) * bpr
-        wn = widen(to_np(w[r:r + 1]))
-        zn = to_np(z[b0:b1])
-        kw = dict(kappa=p.kappa, tau=p.tau, seed=p.seed, step=p.step, tensor_id=9,
-                  block_offset=b0)
-        f = orc.fwd(n, m, wn, zn, **kw)
-        what = f"{n}:{m} row {r}"
-        assert_close(to_np(y[b0:b1]), f["y"], f"{what} y")
-        assert_bf16_ulp(to_np(out[r:r + 1]), f["out"], f"{what} out")
-        h = orc.hard_extract(n, m, zn, 1, cols)
-        assert np.array_equal(to_np(idx[b0:b1]), h["idx"]), what
-        if m == 8:
-            assert np.array_equal(to_np(bits[b0:b1]), h["bits"]), what
-        else:
-            assert np.array_equal(to_np(bits[b0 // 2:b1 // 2]), h["bits"]), what
-        d = orc.bwd(n, m, wn, zn, widen(to_np(G[r:r + 1])), lam=lam, **kw)
-        assert_close(to_np(dz[b0:b1]), d, f"{what} dz")
+    rows_checked = (0, 1, rows // 2, rows - 2, rows - 1)
+    ref = {}
+    # the soft index saved by the forward and read by the backward, then the
+    # benchmark's step: the forward saving nothing and the backward drawing
+    # the soft index again from z (outputs overwritten between the two)
+    for saved in (True, False):
+        mg.maskgs_fwd_hard(t, p, w, z, out, y if saved else None, None, idx, bits)
+        mg.maskgs_bwd(t, p, w, None if saved else z, y if saved else None, G, lam, dz)
+        torch.cuda.synchronize()
+        for r in rows_checked:
+            b0, b1 = r * bpr, (r + 1) * bpr
+            wn = widen(to_np(w[r:r + 1]))
+            zn = to_np(z[b0:b1])
+            kw = dict(kappa=p.kappa, tau=p.tau, seed=p.seed, step=p.step, tensor_id=9,
+                      block_offset=b0)
+            if r not in ref:
+                ref[r] = (orc.fwd(n, m, wn, zn, **kw), orc.hard_extract(n, m, zn, 1, cols),
+                          orc.bwd(n, m, wn, zn, widen(to_np(G[r:r + 1])), lam=lam, **kw))
+            f, h, d = ref[r]
+            what = f"{n}:{m} row {r} ({'saved' if saved else 'recomputed'} soft index)"
+            if saved:
+                assert_close(to_np(y[b0:b1]), f["y"], f"{what} y")
+            assert_bf16_ulp(to_np(out[r:r + 1]), f["out"], f"{what} out")
+            assert np.array_equal(to_np(idx[b0:b1]), h["idx"]), what
+            if m == 8:
+                assert np.array_equal(to_np(bits[b0:b1]), h["bits"]), what
+            else:
+                assert np.array_equal(to_np(bits[b0 // 2:b1 // 2]), h["bits"]), what
+            assert_close(to_np(dz[b0:b1]), d, f"{what} dz")
     del w, G, z, out, y, dz, idx, bits
     torch.cuda.empty_cache()
 

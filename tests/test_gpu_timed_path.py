@@ -16,7 +16,9 @@ section 3.2):
   - soft index, masked weight and logit gradient: on every 61st row plus the
     first and last rows (fp32 within 1e-6 + 1e-5|ref|, bf16 within one ulp).
 The all-linear sweep then checks every one of the 224 tensors the same way on
-sampled rows (integer outputs in full), in groups of four layers.
+sampled rows (integer outputs in full), in groups of four layers, and the
+Nemotron-4-15B-shaped 4:8 layer set goes through its step (the same two calls)
+with the same bars.
 """
 import numpy as np
 import pytest
@@ -112,4 +114,65 @@ def test_all_linear_sweep_sampled(mg, orc, first_layer):
             check_rows(orc, 2, 4, spec, p, w, z, G, wl.lam, None, r["out"], r["dz"], spec.name)
             del w, z, G, r
         print(f"layer {layer}: 7 tensors match the oracle", flush=True)
+        torch.cuda.empty_cache()
+
+
+def _oracle_reg(orc, n, m, spec, p, w, z, chunk_rows=1024):
+    """The oracle regulariser of a whole tensor, summed over row ranges (a row
+    range is a tensor with a block offset, so the noise is the whole
+    tensor's), to keep the oracle's fp64 soft index of a range small."""
+    bpr = spec.cols // m
+    total = 0.0
+    for r0 in range(0, spec.rows, chunk_rows):
+        r1 = min(spec.rows, r0 + chunk_rows)
+        f = orc.fwd(n, m, widen(to_np(w[r0:r1])), to_np(z[r0 * bpr:r1 * bpr]), kappa=p.kappa,
+                    tau=p.tau, seed=p.seed, step=p.step, tensor_id=spec.tensor_id,
+                    block_offset=r0 * bpr)
+        total += f["reg"]
+        del f
+    return total
+
+
+def test_nemotron_step_sampled_rows(mg, orc):
+    """The six Nemotron-shaped 4:8 tensors through the benchmark's step: the
+    fused forward saving no soft index (masked weights, regulariser, argmax,
+    packed bits), then the backward drawing the soft index again; indices and
+    bits in full, the regulariser of each whole tensor within 1e-5, masked
+    weights and dz on sampled rows; the step with the soft index saved gives
+    the same outputs bit for bit."""
+    import torch
+    from workloads import WORKLOADS, tensor_inputs
+    wl = WORKLOADS["nemotron15b_layer_48"]
+    dev = torch.device("cuda:0")
+    p = mg.sample_params(0, 5, wl.kappa, wl.tau)
+    for spec in wl.tensors:
+        w, z, G = tensor_inputs(wl, spec, dev)
+        B = spec.rows * spec.cols // 8
+        t = mg.Tensor(4, 8, spec.rows, spec.cols, 0, spec.tensor_id)
+        res = {}
+        for save_y in (False, True):
+            out = torch.empty_like(w)
+            y = torch.empty_like(z) if save_y else None
+            reg = torch.zeros(1, dtype=torch.float64, device=dev)
+            idx = torch.empty(B, dtype=torch.uint8, device=dev)
+            bits = torch.empty(B, dtype=torch.uint8, device=dev)
+            dz = torch.empty_like(z)
+            mg.maskgs_fwd_hard(t, p, w, z, out, y, reg, idx, bits)
+            mg.maskgs_bwd(t, p, w, None if save_y else z, y, G, wl.lam, dz)
+            torch.cuda.synchronize()
+            res[save_y] = dict(out=out, reg=reg, idx=idx, bits=bits, dz=dz)
+            del y
+        r, rs = res[False], res[True]
+        for k in ("out", "idx", "bits", "dz"):
+            assert torch.equal(r[k], rs[k]), (spec.name, k)
+        del res, rs
+        print(f"{spec.name} {spec.rows}x{spec.cols}: GPU step done", flush=True)
+        h = orc.hard_extract(4, 8, to_np(z), spec.rows, spec.cols)
+        assert np.array_equal(to_np(r["idx"]), h["idx"]), spec.name
+        assert np.array_equal(to_np(r["bits"]), h["bits"]), spec.name
+        del h
+        ref = _oracle_reg(orc, 4, 8, spec, p, w, z)
+        assert abs(r["reg"].item() - ref) <= 1e-5 * ref, (spec.name, r["reg"].item(), ref)
+        check_rows(orc, 4, 8, spec, p, w, z, G, wl.lam, None, r["out"], r["dz"], spec.name)
+        del w, z, G, r
         torch.cuda.empty_cache()
