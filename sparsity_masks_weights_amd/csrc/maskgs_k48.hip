@@ -70,12 +70,16 @@ using C48 = Cands<4, 8>;
 //    1.86 ms on a 24576x6144 tensor and the one saving it 2.33 instead of 2.36;
 //  - backward recomputing the soft index: without accumulation the
 //    register-resident form, 12 waves like the forward (2.54 -> 2.33 ms on
-//    a 24576x6144 tensor against the whole-tile form); with accumulation or
-//    the fused AdamW update the whole-tile form (17920 B tile per wave): 7
-//    waves, one workgroup per CU (150 KB), 3 with accumulation (a second tile);
+//    a 24576x6144 tensor against the whole-tile form; with the fused AdamW
+//    update 7.05 -> 6.79 ms); with accumulation the whole-tile form (17920 B
+//    tile per wave and a second one for the accumulated gradient): 3 waves,
+//    one workgroup per CU;
 //  - the sampled diagnostics (17920 B tile): 7 waves, one per CU.
 constexpr int kNoiseWaves = 12;
 constexpr int kNoiseWgPerCU = 1;
+// Waves per workgroup of bwd48_kernel: one from a saved soft index (the
+// LDS-resident streaming form), else 3 (with accumulation, its only use when
+// the soft index is drawn again) or 7 (one 17920 B tile per wave).
 constexpr int bwd48_waves(bool saved, bool acc) { return saved ? 1 : (acc ? 3 : 7); }
 constexpr int kStatsNoiseWaves = 7;
 
@@ -741,7 +745,7 @@ __device__ __forceinline__ void load8_raw(const void *base, int64_t b, uint4 &r,
 // weights and upstream gradient are requested after the softmax, which keeps
 // them out of the registers the noise needs (requested with the tile they
 // forced 44 bytes of spills per lane).
-template <typename WT, typename GT, bool SAMPLE>
+template <typename WT, typename GT, bool SAMPLE, bool ADAMW>
 __global__ __launch_bounds__(kWave * kNoiseWaves) void bwd48_reg_kernel(BwdArgs a) {
     __shared__ float4 stage4[kNoiseWaves][kHalf * kK / 4];
     __shared__ float4 gtab[kGumbelRows];
@@ -792,7 +796,27 @@ __global__ __launch_bounds__(kWave * kNoiseWaves) void bwd48_reg_kernel(BwdArgs 
                 v[i] = (gscale * v[i]) * t;
             }
         }
-        tile_out(a.dz, b0, nb, stage, v);
+        if (ADAMW) {
+            // each half of the tile's gradient goes through the stage into the
+            // AdamW update of the same logits (coalesced z and moment streams)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int cnt = half_count(nb, h);
+                const int j = lane - h * kHalf;
+                if (j >= 0 && j < cnt) {
+                    float2 *row = reinterpret_cast<float2 *>(stage) + j * (kK / 2);
+#pragma unroll
+                    for (int t2 = 0; t2 < kK / 2; ++t2) row[t2] = make_float2(v[2 * t2], v[2 * t2 + 1]);
+                }
+                wave_sync();
+                const int64_t e0 = (b0 + h * kHalf) * kK;
+                adamw_span<kWave, kHalf * kK / 4, 3>(a.zu + e0, a.m1 + e0, a.m2 + e0, stage,
+                                                     cnt * kK, a.adam, lane);
+                wave_sync();
+            }
+        } else {
+            tile_out(a.dz, b0, nb, stage, v);
+        }
     }
 }
 
@@ -1112,16 +1136,16 @@ hipError_t bwd48_dispatch(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt
 
 // The recomputing backward without accumulation: register-resident, 12-wave
 // workgroups, one per CU.
-template <bool SAMPLE>
+template <bool SAMPLE, bool ADAMW>
 hipError_t bwd48_reg_dispatch(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt,
                               hipStream_t s) {
     const int64_t n = a.g.nblocks;
     const int w = kNoiseWaves, c = kNoiseWgPerCU;
     const bool wb = w_dt == MASKGS_BF16, gb = g_dt == MASKGS_BF16;
-    if (wb && gb) return go_waves(bwd48_reg_kernel<bf16_t, bf16_t, SAMPLE>, a, n, w, c, s);
-    if (wb) return go_waves(bwd48_reg_kernel<bf16_t, float, SAMPLE>, a, n, w, c, s);
-    if (gb) return go_waves(bwd48_reg_kernel<float, bf16_t, SAMPLE>, a, n, w, c, s);
-    return go_waves(bwd48_reg_kernel<float, float, SAMPLE>, a, n, w, c, s);
+    if (wb && gb) return go_waves(bwd48_reg_kernel<bf16_t, bf16_t, SAMPLE, ADAMW>, a, n, w, c, s);
+    if (wb) return go_waves(bwd48_reg_kernel<bf16_t, float, SAMPLE, ADAMW>, a, n, w, c, s);
+    if (gb) return go_waves(bwd48_reg_kernel<float, bf16_t, SAMPLE, ADAMW>, a, n, w, c, s);
+    return go_waves(bwd48_reg_kernel<float, float, SAMPLE, ADAMW>, a, n, w, c, s);
 }
 
 hipError_t launch_bwd48(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, hipStream_t s) {
@@ -1129,16 +1153,16 @@ hipError_t launch_bwd48(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, 
     const bool smp = a.nz.hard_sample && !a.y;
     if (a.m1) {  // fused AdamW update (never with accumulation)
         if (a.y) return bwd48_dispatch<true, false, true, false>(a, w_dt, g_dt, s);
-        return smp ? bwd48_dispatch<false, false, true, true>(a, w_dt, g_dt, s)
-                   : bwd48_dispatch<false, false, true, false>(a, w_dt, g_dt, s);
+        return smp ? bwd48_reg_dispatch<true, true>(a, w_dt, g_dt, s)
+                   : bwd48_reg_dispatch<false, true>(a, w_dt, g_dt, s);
     }
     if (a.y) return a.accumulate ? bwd48_dispatch<true, true, false, false>(a, w_dt, g_dt, s)
                                  : bwd48_dispatch<true, false, false, false>(a, w_dt, g_dt, s);
     if (a.accumulate)
         return smp ? bwd48_dispatch<false, true, false, true>(a, w_dt, g_dt, s)
                    : bwd48_dispatch<false, true, false, false>(a, w_dt, g_dt, s);
-    return smp ? bwd48_reg_dispatch<true>(a, w_dt, g_dt, s)
-               : bwd48_reg_dispatch<false>(a, w_dt, g_dt, s);
+    return smp ? bwd48_reg_dispatch<true, false>(a, w_dt, g_dt, s)
+               : bwd48_reg_dispatch<false, false>(a, w_dt, g_dt, s);
 }
 
 hipError_t launch_reg48(const RegArgs &a, maskgs_dtype w_dt, hipStream_t s) {
