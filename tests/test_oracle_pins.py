@@ -804,3 +804,47 @@ def test_hard_sample_forward_and_straight_through(orc, nm):
     d_hard = orc.bwd(n, m, w, z, G, lam=0.5, flags=orc.HARD_SAMPLE, **kw)
     assert not np.array_equal(d_hard, orc.bwd(n, m, w, z, G, lam=0.5, **kw))
     assert np.abs(d_hard.sum(axis=1)).max() <= 1e-12 * np.abs(d_hard).max()  # sum_i dz_i = 0
+
+
+@pytest.mark.parametrize("nm,lam,with_g", [((2, 4), 0.25, True), ((4, 8), 0.25, True),
+                                            ((2, 4), 0.5, False), ((4, 8), 0.5, False)])
+def test_hard_sample_backward_is_straight_through_autograd(orc, nm, lam, with_g):
+    """The hard-sample backward against torch autograd of the straight-through
+    estimator written out: the applied mask is M_h + M~ - stopgrad(M~), so
+    L = sum G.(W.M) - lambda sum (W.M)^2 takes its value at the hard mask M_h
+    and its gradient through the soft mask M~ = softmax(a) S.  The perturbed,
+    tempered logits a come from the oracle (they fix the noise) and depend on z
+    with slope kappa/tau; M_h is read off the oracle's hard-sample forward.
+    A soft mask in the regulariser term, a lost factor 2, a flipped sign of
+    lambda or a missing kappa/tau all fail this."""
+    import torch
+    n, m = nm
+    rng = np.random.default_rng(41 + m)
+    K = math.comb(m, n)
+    rows, cols = 8, 8 * m
+    w = rng.normal(0, 1.0, size=(rows, cols)).astype(np.float32)
+    z = rng.normal(0, 0.05, size=(rows * cols // m, K)).astype(np.float32)
+    G = (rng.normal(0, 1.0, size=(rows, cols)) if with_g else np.zeros((rows, cols))).astype(np.float32)
+    kappa, tau = 3.0, 1.5
+    kw = dict(kappa=kappa, tau=tau, seed=7, step=2, tensor_id=1, block_offset=3)
+    a = orc.sample_logits(n, m, z, rows, cols, **kw).astype(np.float64)
+    hard = orc.fwd(n, m, w, z, out_dtype="f32", flags=orc.HARD_SAMPLE, **kw)
+    mh = (hard["out"].reshape(-1, m) != 0).astype(np.float64)
+    cands = orc.candidates(n, m).astype(np.int64)
+    S = torch.tensor((cands[:, None] >> np.arange(m)) & 1, dtype=torch.float64)
+    zt = torch.tensor(z.astype(np.float64), requires_grad=True)
+    slope = kappa / tau
+    at = zt * slope + torch.tensor(a - z.astype(np.float64) * slope)
+    ms = torch.softmax(at, dim=1) @ S
+    mst = torch.tensor(mh) + ms - ms.detach()
+    u = torch.tensor(w.astype(np.float64).reshape(-1, m)) * mst
+    L = (torch.tensor(G.astype(np.float64).reshape(-1, m)) * u).sum() - lam * (u * u).sum()
+    L.backward()
+    ref = zt.grad.numpy()
+    d = orc.bwd(n, m, w, z, G, lam=lam, flags=orc.HARD_SAMPLE, **kw)
+    scale = np.abs(ref).max()
+    assert scale > 0
+    assert np.abs(d - ref).max() <= 1e-6 * scale
+    # the soft regulariser term gives a different gradient on these inputs
+    d_soft = orc.bwd(n, m, w, z, G, lam=lam, **kw)
+    assert np.abs(d_soft - ref).max() > 1e-3 * scale
