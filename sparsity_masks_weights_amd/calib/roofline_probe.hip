@@ -157,13 +157,31 @@ enum Op {
     kExpF32,       // v_exp_f32 v, v
     kRcpF32,       // v_rcp_f32 v, v
     kFmaF64,       // v_fma_f64 v[2], v[2], v[2], v[2]
+    kBitop3Sgpr,   // v_bitop3_b32 v, v, v, s (one scalar operand)
+    kCndmaskVcc,   // v_cndmask_b32 v, v, v, vcc
+    kCmpVcc,       // v_cmp_gt_f32 vcc, v, v
+    kMovSgpr,      // v_mov_b32 v, s
+    kMax3F32,      // v_max3_f32 v, v, v, v
+    kMin3U32,      // v_min3_u32 v, v, v, v
+    kAndOrB32,     // v_and_or_b32 v, v, v, v
+    kOrLiteral,    // v_or_b32 v, literal, v
+    kCmpCndmask,   // v_cmp_gt_f32 vcc, v, v then v_cndmask_b32 v, v, v, vcc (a pair)
+    kCndmaskSgpr,  // v_cndmask_b32 v, v, v, s[2] (VOP3 form, mask in a scalar pair)
+    kMaxF32,       // v_max_f32 v, v, v
+    kMulF32,       // v_mul_f32 v, v, v
+    kBfiB32,       // v_bfi_b32 v, v, v, v
     kNumOps
 };
 
 const char *op_name(int op) {
     static const char *names[] = {"v_add_u32 (vgpr)",  "v_fma_f32 (vgpr)", "v_fma_f32 (sgpr)",
                                   "v_bitop3_b32",      "v_mad_u64_u32",    "v_cvt_f32_u32",
-                                  "v_exp_f32",         "v_rcp_f32",        "v_fma_f64"};
+                                  "v_exp_f32",         "v_rcp_f32",        "v_fma_f64",
+                                  "v_bitop3_b32 (sgpr)", "v_cndmask_b32 (vcc)", "v_cmp_gt_f32 (vcc)",
+                                  "v_mov_b32 (sgpr)",  "v_max3_f32",       "v_min3_u32",
+                                  "v_and_or_b32",      "v_or_b32 (literal)",
+                                  "cmp+cndmask (vcc)", "v_cndmask_b32 (s[2])", "v_max_f32",
+                                  "v_mul_f32",         "v_bfi_b32"};
     return names[op];
 }
 
@@ -209,6 +227,39 @@ __global__ __launch_bounds__(kThreads) void valu_kernel(uint32_t *sink, uint32_t
             if constexpr (OP == kRcpF32) asm volatile("v_rcp_f32 %0, %0" : "+v"(f[c]));
             if constexpr (OP == kFmaF64)
                 asm volatile("v_fma_f64 %0, %0, %1, %2" : "+v"(d[c]) : "v"(da), "v"(db));
+            if constexpr (OP == kBitop3Sgpr)
+                asm volatile("v_bitop3_b32 %0, %0, %1, %2 bitop3:0x96"
+                             : "+v"(u[c])
+                             : "v"(ku), "s"(seed));
+            if constexpr (OP == kCndmaskVcc)
+                asm volatile("v_cndmask_b32 %0, %0, %1, vcc" : "+v"(u[c]) : "v"(ku));
+            if constexpr (OP == kCmpVcc)
+                asm volatile("v_cmp_gt_f32 vcc, %0, %1" : : "v"(f[c]), "v"(fa) : "vcc");
+            if constexpr (OP == kMovSgpr)
+                asm volatile("v_mov_b32 %0, %1" : "=v"(u[c]) : "s"(seed + static_cast<uint32_t>(c)));
+            if constexpr (OP == kMax3F32)
+                asm volatile("v_max3_f32 %0, %0, %1, %2" : "+v"(f[c]) : "v"(fa), "v"(fb));
+            if constexpr (OP == kMin3U32)
+                asm volatile("v_min3_u32 %0, %0, %1, %2" : "+v"(u[c]) : "v"(ku), "v"(kv));
+            if constexpr (OP == kAndOrB32)
+                asm volatile("v_and_or_b32 %0, %0, %1, %2" : "+v"(u[c]) : "v"(ku), "v"(kv));
+            if constexpr (OP == kOrLiteral)
+                asm volatile("v_or_b32 %0, 0x12345, %0" : "+v"(u[c]));
+            if constexpr (OP == kCmpCndmask)
+                asm volatile("v_cmp_gt_f32 vcc, %1, %2\n\tv_cndmask_b32 %0, %0, %3, vcc"
+                             : "+v"(u[c])
+                             : "v"(f[c]), "v"(fa), "v"(ku)
+                             : "vcc");
+            if constexpr (OP == kCndmaskSgpr)
+                asm volatile("v_cndmask_b32_e64 %0, %0, %1, %2"
+                             : "+v"(u[c])
+                             : "v"(ku), "s"(static_cast<uint64_t>(seed) * 0x9E3779B97F4A7C15ull));
+            if constexpr (OP == kMaxF32)
+                asm volatile("v_max_f32 %0, %0, %1" : "+v"(f[c]) : "v"(fa));
+            if constexpr (OP == kMulF32)
+                asm volatile("v_mul_f32 %0, %0, %1" : "+v"(f[c]) : "v"(fa));
+            if constexpr (OP == kBfiB32)
+                asm volatile("v_bfi_b32 %0, %1, %0, %2" : "+v"(u[c]) : "v"(ku), "v"(kv));
         }
     }
     uint32_t r = 0;
@@ -386,7 +437,7 @@ void valu_one(uint32_t *sink, unsigned grid) {
     const double ms = best_ms(
         [&](unsigned gr) { valu_kernel<OP><<<gr, kThreads>>>(sink, 1u, 0.9999f); }, {grid}, 3, &g);
     const double waves = static_cast<double>(grid) * (kThreads / 64);
-    const double insts = waves * kChains * kIters;
+    const double insts = waves * kChains * kIters * (OP == kCmpCndmask ? 2 : 1);
     const double rate = insts / (ms * 1e3);  // wave instructions per microsecond
     std::printf("%-20s %9.1f us  %8.1f k wave-instr/us  %.2f cycles per instruction per SIMD "
                 "at 2.4 GHz\n",
