@@ -136,22 +136,49 @@ struct Elem<bf16_t> {
 // The draw: keys a_j = fp32(pi_j + g_j) (g_j from Philox word gb*M + j), then
 // N rounds of "first largest key among the positions not yet drawn" (strict
 // '>' from the lowest position, so ties and NaN keys go to the lower one).
-// gtab: the noise contract's coefficient table in LDS.
+// The draw is returned as ranks: rank_j = k for the position drawn in round k
+// (k < N); every position not drawn has a rank >= N.
+// gtab: the noise coefficient table in LDS.
 // ---------------------------------------------------------------------------
-template <int N, int M>
-__device__ __forceinline__ uint32_t draw(const float (&p)[M], uint64_t gb, const MpArgs &a,
-                                         const float4 *gtab, int (&ord)[N]) {
-    float key[M];
-    if (a.no_noise) {
+
+// For keys that are neither NaN nor infinite the rounds order the positions
+// by key, larger first and equal keys lower position first, so
+//   rank_j = #{l < j : key_l >= key_j} + #{l > j : key_l > key_j}.
+// Every pair l < j contributes one sign bit, that of key_l - key_j, set
+// exactly when key_j > key_l (the keys have -0 turned into +0 first, so equal
+// keys differ by +0): then j goes before l.  Three dual-issue instructions per
+// pair instead of a compare and selects per position and round.  Returns
+// false if some key is NaN or infinite (the caller then runs the rounds).
+template <int M>
+__device__ __forceinline__ bool ranks_by_key(const float (&key)[M], uint32_t (&rank)[M]) {
+    float k[M];
+    float probe = 0.0f;
 #pragma unroll
-        for (int j = 0; j < M; ++j) key[j] = p[j];
-    } else {
-        uint32_t wd[M];
-        stream_words<M, 0>(gb * static_cast<uint64_t>(M / 4), a.step, a.tensor_id, a.k0, a.k1,
-                           wd);
-#pragma unroll
-        for (int j = 0; j < M; ++j) key[j] = p[j] + gumbel_lds(wd[j], gtab);
+    for (int j = 0; j < M; ++j) {
+        k[j] = key[j] + 0.0f;
+        probe = __builtin_fmaf(k[j], 0.0f, probe);  // NaN iff some key is NaN or infinite
     }
+    uint32_t after[M], before[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) after[j] = before[j] = 0u;
+#pragma unroll
+    for (int j = 1; j < M; ++j) {
+#pragma unroll
+        for (int l = 0; l < j; ++l) {
+            const uint32_t g = f32_to_bits(k[l] - k[j]) >> 31;  // key_j > key_l
+            after[j] += g;   // l that j goes before, among l < j
+            before[l] += g;  // j that go before l, among j > l
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < M; ++j) rank[j] = static_cast<uint32_t>(j) - after[j] + before[j];
+    return probe == 0.0f;
+}
+
+// The rounds themselves: ord[k] is the position drawn in round k.
+template <int N, int M>
+__device__ __forceinline__ void draw_rounds(const float (&key)[M], uint32_t (&rank)[M]) {
+    int ord[N];
     uint32_t taken = 0;
 #pragma unroll
     for (int k = 0; k < N; ++k) {
@@ -166,15 +193,45 @@ __device__ __forceinline__ uint32_t draw(const float (&p)[M], uint64_t gb, const
         ord[k] = best;
         taken |= 1u << best;
     }
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+        uint32_t r = N;
+#pragma unroll
+        for (int k = 0; k < N; ++k) r = (ord[k] == j) ? static_cast<uint32_t>(k) : r;
+        rank[j] = r;
+    }
+}
+
+// Returns the packed set of drawn positions (bit j = position j drawn).
+template <int N, int M>
+__device__ __forceinline__ uint32_t draw(const float (&p)[M], uint64_t gb, const MpArgs &a,
+                                         const float4 *gtab, uint32_t (&rank)[M]) {
+    float key[M];
+    if (a.no_noise) {
+#pragma unroll
+        for (int j = 0; j < M; ++j) key[j] = p[j];
+    } else {
+        uint32_t wd[M];
+        stream_words<M, 0>(gb * static_cast<uint64_t>(M / 4), a.step, a.tensor_id, a.k0, a.k1,
+                           wd);
+#pragma unroll
+        for (int j = 0; j < M; ++j) key[j] = p[j] + gumbel_lds(wd[j], gtab);
+    }
+    if (!ranks_by_key<M>(key, rank)) draw_rounds<N, M>(key, rank);
+    uint32_t taken = 0;
+#pragma unroll
+    for (int j = 0; j < M; ++j) taken |= (rank[j] < static_cast<uint32_t>(N) ? 1u : 0u) << j;
     return taken;
 }
 
+// Draw order packed kBits per round, round 0 lowest.
 template <int N, int M>
-__device__ __forceinline__ uint32_t pack_order(const int (&ord)[N]) {
-    constexpr int kBits = (M == 4) ? 2 : 3;
+__device__ __forceinline__ uint32_t pack_order(const uint32_t (&rank)[M]) {
+    constexpr uint32_t kBits = (M == 4) ? 2 : 3;
     uint32_t v = 0;
 #pragma unroll
-    for (int k = 0; k < N; ++k) v |= static_cast<uint32_t>(ord[k]) << (kBits * k);
+    for (int j = 0; j < M; ++j)
+        v |= rank[j] < static_cast<uint32_t>(N) ? static_cast<uint32_t>(j) << (kBits * rank[j]) : 0u;
     return v;
 }
 
@@ -197,8 +254,8 @@ __global__ __launch_bounds__(kThreads) void mp_fwd_kernel(MpArgs a) {
         if (live) {
             float p[M];
             BlockIo<float, M>::load(a.pi, b, p);
-            int ord[N];
-            keep = draw<N, M>(p, a.block_offset + static_cast<uint64_t>(b), a, gtab, ord);
+            uint32_t rank[M];
+            keep = draw<N, M>(p, a.block_offset + static_cast<uint64_t>(b), a, gtab, rank);
             if (a.out) {
                 uint32_t r[M], o[M];
                 BlockIo<WT, M>::load_raw(a.w, b, r);
@@ -212,10 +269,10 @@ __global__ __launch_bounds__(kThreads) void mp_fwd_kernel(MpArgs a) {
             }
             if (a.order) {
                 if (M == 4)
-                    static_cast<uint8_t *>(a.order)[b] = static_cast<uint8_t>(pack_order<N, M>(ord));
+                    static_cast<uint8_t *>(a.order)[b] = static_cast<uint8_t>(pack_order<N, M>(rank));
                 else
                     static_cast<uint16_t *>(a.order)[b] =
-                        static_cast<uint16_t>(pack_order<N, M>(ord));
+                        static_cast<uint16_t>(pack_order<N, M>(rank));
             }
         }
         if (a.bits) {
@@ -247,7 +304,10 @@ template <int N, int M, bool ORDER_IN>
 __device__ __forceinline__ void mp_bwd_block(const MpArgs &a, int64_t b, const float4 *gtab) {
     float q[M];
     BlockIo<float, M>::load(a.pi, b, q);
+    // the position closed after round k: ord[k] from the saved order, or the
+    // one of rank k from the draw
     int ord[N];
+    uint32_t rank[M];
     if (ORDER_IN) {
         constexpr int kBits = (M == 4) ? 2 : 3;
         const uint32_t v = (M == 4) ? static_cast<const uint8_t *>(a.order_in)[b]
@@ -255,12 +315,11 @@ __device__ __forceinline__ void mp_bwd_block(const MpArgs &a, int64_t b, const f
 #pragma unroll
         for (int k = 0; k < N; ++k) ord[k] = (v >> (kBits * k)) & ((1u << kBits) - 1u);
     } else {
-        draw<N, M>(q, a.block_offset + static_cast<uint64_t>(b), a, gtab, ord);
+        draw<N, M>(q, a.block_offset + static_cast<uint64_t>(b), a, gtab, rank);
     }
     float acc[M];
 #pragma unroll
     for (int j = 0; j < M; ++j) acc[j] = 0.0f;
-    uint32_t taken = 0;
 #pragma unroll
     for (int k = 0; k < N; ++k) {
         float mx = q[0];
@@ -280,15 +339,26 @@ __device__ __forceinline__ void mp_bwd_block(const MpArgs &a, int64_t b, const f
         const float inv = __builtin_amdgcn_rcpf(z);
 #pragma unroll
         for (int l = 0; l < M; ++l) acc[l] = __builtin_fmaf(-e[l], inv, acc[l]);
-        const int jk = ord[k];
-        taken |= 1u << jk;
         if (k + 1 < N) {
 #pragma unroll
-            for (int l = 0; l < M; ++l) q[l] = (l == jk) ? -__builtin_huge_valf() : q[l];
+            for (int l = 0; l < M; ++l) {
+                const bool closed = ORDER_IN ? l == ord[k] : rank[l] == static_cast<uint32_t>(k);
+                q[l] = closed ? -__builtin_huge_valf() : q[l];
+            }
         }
     }
 #pragma unroll
-    for (int l = 0; l < M; ++l) acc[l] += ((taken >> l) & 1u) ? 1.0f : 0.0f;
+    for (int l = 0; l < M; ++l) {
+        bool drawn;
+        if (ORDER_IN) {
+            drawn = false;
+#pragma unroll
+            for (int k = 0; k < N; ++k) drawn = drawn || l == ord[k];
+        } else {
+            drawn = rank[l] < static_cast<uint32_t>(N);
+        }
+        acc[l] += drawn ? 1.0f : 0.0f;
+    }
     float d[M];
     if (a.accumulate) {
         BlockIo<float, M>::load(a.dpi, b, d);

@@ -172,6 +172,51 @@ def test_no_noise_draw_and_extreme_logits(mg, orc, n, m):
         assert_pg(to_np(d), ref, 1.0, n, f"flags {flags}")
 
 
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
+def test_draw_special_keys(mg, orc, n, m):
+    """The draw where keys are NaN, infinite, signed zeros or equal: the order
+    is the oracle's scan (strict '>' from the lowest open position, so equal
+    keys and a NaN at the first open position keep the lower position) bit for
+    bit, with and without noise, and the gradient drawing again equals the one
+    from the saved order (NaN where the logits make it NaN)."""
+    import torch
+    nan, inf = np.float32(np.nan), np.float32(np.inf)
+    rng = np.random.default_rng(40 + m)
+    pats = [[nan] + [1.0] * (m - 1), [1.0, 2.0, nan] + [0.5] * (m - 3), [nan] * m,
+            [inf] + [0.0] * (m - 1), [0.0, inf, 1.0, inf] + [2.0] * (m - 4), [-inf] * m,
+            [-inf, 0.0] + [-inf] * (m - 2), [inf, -inf] * (m // 2), [inf] * m,
+            [-0.0, 0.0, -0.0, 0.0] + [-1.0] * (m - 4), [0.0, -0.0] * (m // 2),
+            [-0.0] * m, [3.0] * m, [1.0, 3.0, 3.0, 1.0] * (m // 4)]
+    # every pattern in several rotations, then ordinary blocks
+    blocks = [np.roll(np.array(p, np.float32), r) for p in pats for r in range(0, m, 3)]
+    blocks += list(rng.standard_normal((64, m)).astype(np.float32))
+    pin = np.stack(blocks).astype(np.float32)
+    pad = (-len(pin)) % 4
+    pin = np.concatenate([pin, rng.standard_normal((pad, m)).astype(np.float32)])
+    B = len(pin)
+    rows, cols = B // 4, 4 * m
+    pi = torch.from_numpy(pin).cuda()
+    t = mg.Tensor(n, m, rows, cols, 0, 2)
+    for flags in (mg.MASKGS_NO_NOISE, 0):
+        p = mg.draw_params(13, 5, flags)
+        order = _order_tensor(B, m, pi.device)
+        bits = torch.empty((B * m + 7) // 8, dtype=torch.uint8, device=pi.device)
+        mg.maskpro_fwd(t, p, pi, mask_bits=bits, order=order)
+        d_saved = torch.empty_like(pi)
+        d_redrawn = torch.empty_like(pi)
+        mg.maskpro_bwd(t, p, pi, 1.0, d_saved, order=order)
+        mg.maskpro_bwd(t, p, pi, 1.0, d_redrawn)
+        torch.cuda.synchronize()
+        kw = dict(seed=13, step=5, tensor_id=2, flags=flags)
+        f = orc.maskpro_fwd(n, m, np.ones((rows, cols), np.float32), pin, **kw)
+        assert np.array_equal(order_np(order, m), pack_order(f["order"], m)), flags
+        assert np.array_equal(to_np(bits), f["bits"]), flags
+        np.testing.assert_array_equal(to_np(d_redrawn), to_np(d_saved))
+        fin = np.isfinite(pin).all(axis=1)
+        ref = orc.maskpro_grad(n, m, pin, rows, cols, advantage=1.0, **kw)
+        assert_pg(to_np(d_redrawn)[fin], ref[fin], 1.0, n, f"finite blocks, flags {flags}")
+
+
 @pytest.mark.parametrize("n,m,source", [(2, 4, "bits"), (2, 4, "w_bf16"), (4, 8, "w_f32"),
                                         (4, 8, "bits"), (2, 4, "w_f32")])
 def test_init(mg, orc, n, m, source):
