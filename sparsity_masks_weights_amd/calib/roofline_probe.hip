@@ -55,7 +55,18 @@ __device__ __forceinline__ uint32_t fold4(float4 v) {
 // result is kept live by a store that happens only if the running xor equals
 // a fixed constant (practically never): no write traffic.
 // ---------------------------------------------------------------------------
-template <int U>
+// A float4 load, non-temporal (NTL) or plain.
+template <bool NTL>
+__device__ __forceinline__ float4 load4(const float4 *p) {
+    if constexpr (NTL) {
+        const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(p));
+        return make_float4(v.x, v.y, v.z, v.w);
+    } else {
+        return *p;
+    }
+}
+
+template <int U, bool NTL = false>
 __global__ __launch_bounds__(kThreads) void read_kernel(const float4 *src, int64_t n4,
                                                         uint32_t *sink) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads * U;
@@ -65,7 +76,8 @@ __global__ __launch_bounds__(kThreads) void read_kernel(const float4 *src, int64
         float4 v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            v[u] = i0 + u * kThreads < n4 ? src[i0 + u * kThreads] : make_float4(0, 0, 0, 0);
+            v[u] = i0 + u * kThreads < n4 ? load4<NTL>(src + i0 + u * kThreads)
+                                          : make_float4(0, 0, 0, 0);
 #pragma unroll
         for (int u = 0; u < U; ++u) acc ^= fold4(v[u]);
     }
@@ -87,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void write_kernel(float4 *dst, int64_t n4
 
 // Copy, U float4 per lane in flight per iteration (loads first, then stores);
 // non-temporal or plain stores.  Every access is bounds-checked.
-template <int U, bool NT>
+template <int U, bool NT, bool NTL = false>
 __global__ __launch_bounds__(kThreads) void copy_kernel(const float4 *src, float4 *dst,
                                                         int64_t n4) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads * U;
@@ -96,7 +108,8 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const float4 *src, float
         float4 v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            v[u] = i0 + u * kThreads < n4 ? src[i0 + u * kThreads] : make_float4(0, 0, 0, 0);
+            v[u] = i0 + u * kThreads < n4 ? load4<NTL>(src + i0 + u * kThreads)
+                                          : make_float4(0, 0, 0, 0);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (i0 + u * kThreads >= n4) continue;
@@ -352,6 +365,9 @@ void run_hbm() {
     ms = best_ms([&](unsigned gr) { read_kernel<4><<<gr, kThreads>>>(a, n4, sink); }, grids, 5,
                  &g);
     report("read (4 in flight per lane)", static_cast<double>(bytes), ms, g);
+    ms = best_ms([&](unsigned gr) { read_kernel<1, true><<<gr, kThreads>>>(a, n4, sink); }, grids,
+                 5, &g);
+    report("read (non-temporal loads)", static_cast<double>(bytes), ms, g);
     ms = best_ms([&](unsigned gr) { write_kernel<false><<<gr, kThreads>>>(b, n4); }, grids, 5, &g);
     report("write", static_cast<double>(bytes), ms, g);
     ms = best_ms([&](unsigned gr) { write_kernel<true><<<gr, kThreads>>>(b, n4); }, grids, 5, &g);
@@ -371,6 +387,12 @@ void run_hbm() {
         ms = best_ms([&](unsigned gr) { copy_kernel<4, false><<<gr, kThreads>>>(a, b, h4); },
                      grids, 5, &g);
         report("copy (4 in flight, plain stores)", 2.0 * 16 * h4, ms, g);
+        ms = best_ms([&](unsigned gr) { copy_kernel<1, true, true><<<gr, kThreads>>>(a, b, h4); },
+                     grids, 5, &g);
+        report("copy (nt loads, nt stores)", 2.0 * 16 * h4, ms, g);
+        ms = best_ms([&](unsigned gr) { copy_kernel<1, false, true><<<gr, kThreads>>>(a, b, h4); },
+                     grids, 5, &g);
+        report("copy (nt loads, plain stores)", 2.0 * 16 * h4, ms, g);
         ms = best_ms(
             [&](unsigned) { CHECK(hipMemcpyAsync(b, a, 16 * h4, hipMemcpyDeviceToDevice, 0)); },
             {0u}, 5, &g);
