@@ -597,22 +597,27 @@ __global__ __launch_bounds__(kWave * kNoiseWaves) void reg48_noise_kernel(RegArg
 // in each pass instead of being kept in registers across passes.
 __device__ __forceinline__ void row_pass_barrier() { asm volatile("" ::: "memory"); }
 
-// Kept and dropped positions of every candidate, ascending: kPos.p[i][k] is
-// the k-th set bit of S_i, kPos.c[i][k] the k-th clear one.  A compile-time
-// table, so unrolled uses fold to constants.
-struct PosTable {
-    uint8_t p[kK][4], c[kK][4];
-    constexpr PosTable() : p(), c() {
-        for (int i = 0; i < kK; ++i) {
-            int k = 0, n = 0;
-            for (int j = 0; j < 8; ++j) {
-                if ((C48::at(i) >> j) & 1u) p[i][k++] = static_cast<uint8_t>(j);
-                else c[i][n++] = static_cast<uint8_t>(j);
-            }
-        }
+// t_i = sum_{j in S_i} pk_j - sum_{j not in S_i} qd_j for every candidate, by
+// halves: with x_j = pk_j where the candidate keeps position j and -qd_j where
+// it drops it, R_lo(A) sums x_j over positions 0-3 for the low-half pattern A
+// and R_hi(B) over 4-7, both from the sums of their two position pairs (four
+// patterns per pair), and t_i = R_lo(lo_i) + R_hi(hi_i): 118 additions for
+// the 70 terms instead of 266 from pair sums.
+__device__ __forceinline__ void half_terms(const float (&pk)[8], const float (&qd)[8], int base,
+                                           float (&R)[16]) {
+    float P0[4], P1[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float a0 = (p & 1) ? pk[base] : -qd[base];
+        const float a1 = (p & 2) ? pk[base + 1] : -qd[base + 1];
+        const float b0 = (p & 1) ? pk[base + 2] : -qd[base + 2];
+        const float b1 = (p & 2) ? pk[base + 3] : -qd[base + 3];
+        P0[p] = a0 + a1;
+        P1[p] = b0 + b1;
     }
-};
-constexpr PosTable kPos{};
+#pragma unroll
+    for (int A = 0; A < 16; ++A) R[A] = P0[A & 3] + P1[A >> 2];
+}
 
 // Backward (section 3.2 information flow; section 3.4 Eq. 8), fp32:
 // dm_j = G_j w_j - 2 lambda w_j (w_j m_j); dz_i = (kappa/tau) y_i (dy_i - s)
@@ -683,14 +688,12 @@ __global__ __launch_bounds__(kWave * bwd48_waves(SAVED, ACC)) void bwd48_kernel(
             }
             row_pass_barrier();
             const float *prow = pv + lane * kK;
+            float Rlo[16], Rhi[16];
+            half_terms(pk, qd, 0, Rlo);
+            half_terms(pk, qd, 4, Rhi);
 #pragma unroll
             for (int i = 0; i < kK; ++i) {
-                // (pair + pair) sums over S_i and its complement; the pair sums
-                // are shared between candidates
-                const float t = ((pk[kPos.p[i][0]] + pk[kPos.p[i][1]]) +
-                                 (pk[kPos.p[i][2]] + pk[kPos.p[i][3]])) -
-                                ((qd[kPos.c[i][0]] + qd[kPos.c[i][1]]) +
-                                 (qd[kPos.c[i][2]] + qd[kPos.c[i][3]]));
+                const float t = Rlo[kSplit.lo[i]] + Rhi[kSplit.hi[i]];
                 const float sy = gscale * row[i];
                 row[i] = ACC ? __builtin_fmaf(sy, t, prow[i]) : sy * t;
             }
@@ -787,12 +790,12 @@ __global__ __launch_bounds__(kWave * kNoiseWaves) void bwd48_reg_kernel(BwdArgs 
                 pk[j] = mb[j] * dm;
                 qd[j] = m[j] * dm;
             }
+            float Rlo[16], Rhi[16];
+            half_terms(pk, qd, 0, Rlo);
+            half_terms(pk, qd, 4, Rhi);
 #pragma unroll
             for (int i = 0; i < kK; ++i) {
-                const float t = ((pk[kPos.p[i][0]] + pk[kPos.p[i][1]]) +
-                                 (pk[kPos.p[i][2]] + pk[kPos.p[i][3]])) -
-                                ((qd[kPos.c[i][0]] + qd[kPos.c[i][1]]) +
-                                 (qd[kPos.c[i][2]] + qd[kPos.c[i][3]]));
+                const float t = Rlo[kSplit.lo[i]] + Rhi[kSplit.hi[i]];
                 v[i] = (gscale * v[i]) * t;
             }
         }
