@@ -35,6 +35,14 @@ constexpr int kWgPerCU = MASKGS_K24_WG_PER_CU;  // grid cap: workgroups of kThre
 // prior seeding 16.8 -> 15.8 ms, training backward 46.8 -> 45.6 ms; the
 // forward and the plain backward measured best at 8.
 constexpr int kWgPerCUStream = 64;
+// Lanes per workgroup and grid cap of the backward that draws the soft index
+// again (without the fused update): 1024-lane workgroups, one resident per CU
+// (72 KB of LDS, 75 registers), took the 7B step's backward phase from 18.8
+// to 18.3 ms against 512-lane ones (grid caps of 2, 4 and 8 per CU within
+// 0.5% of each other).  The forward measured within 1% of 512 lanes at 256
+// and 768, and keeps kThreads.
+constexpr int kBwdRcThreads = 1024;
+constexpr int kBwdRcWgPerCU = 4;
 using C24 = Cands<2, 4>;
 
 // ---------------------------------------------------------------------------
@@ -577,19 +585,19 @@ __device__ __forceinline__ void soft_mask4_complement(const float *y, float *mb)
     }
 }
 
-template <int PHASE, typename WT, typename GT, bool SAVED, bool ADAMW>
-__global__ __launch_bounds__(kThreads) void bwd24_kernel(BwdArgs a) {
-    __shared__ float4 stage[3 * kThreads];
+template <int PHASE, typename WT, typename GT, bool SAVED, bool ADAMW, int T>
+__global__ __launch_bounds__(T) void bwd24_kernel(BwdArgs a) {
+    __shared__ float4 stage[3 * T];
     __shared__ float4 gtab[SAVED ? 1 : kGumbelRows];
     if constexpr (!SAVED) {
-        load_gumbel_table<kThreads>(gtab);
+        load_gumbel_table<T>(gtab);
         __syncthreads();
     }
     const int64_t npairs = (a.g.nblocks + 1) >> 1;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * T;
     const float two_lambda = static_cast<float>(2.0 * a.lambda);
     const float gscale = static_cast<float>(a.nz.grad_scale);
-    for (int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads; base < npairs;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * T; base < npairs;
          base += stride) {
         const int64_t p = base + threadIdx.x;
         float dz[12];
@@ -932,11 +940,11 @@ __global__ __launch_bounds__(kThreads) void stats24_kernel(StatsArgs a) {
                   static_cast<unsigned long long>(a.g.nblocks));
 }
 
-template <typename K, typename A>
+template <int T = kThreads, typename K, typename A>
 hipError_t go(K kernel, const A &args, int64_t items, hipStream_t s,
               int wg_per_cu = kWgPerCU) {
-    const unsigned grid = grid_for(items, kThreads, wg_per_cu);
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, s, args);
+    const unsigned grid = grid_for(items, T, wg_per_cu);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(T), 0, s, args);
     return hipGetLastError();
 }
 
@@ -964,14 +972,16 @@ hipError_t fwd24_dispatch(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype o_dt
 template <int PHASE, bool SAVED, bool ADAMW>
 hipError_t bwd24_dispatch(const BwdArgs &a, maskgs_dtype w_dt, maskgs_dtype g_dt, hipStream_t s) {
     const int64_t np = (a.g.nblocks + 1) >> 1;
-    const int c = ADAMW ? kWgPerCUStream : kWgPerCU;
+    constexpr bool rc = !SAVED && !ADAMW;
+    constexpr int T = rc ? kBwdRcThreads : kThreads;
+    const int c = ADAMW ? kWgPerCUStream : (rc ? kBwdRcWgPerCU : kWgPerCU);
     if (w_dt == MASKGS_BF16 && g_dt == MASKGS_BF16)
-        return go(bwd24_kernel<PHASE, bf16_t, bf16_t, SAVED, ADAMW>, a, np, s, c);
+        return go<T>(bwd24_kernel<PHASE, bf16_t, bf16_t, SAVED, ADAMW, T>, a, np, s, c);
     if (w_dt == MASKGS_BF16)
-        return go(bwd24_kernel<PHASE, bf16_t, float, SAVED, ADAMW>, a, np, s, c);
+        return go<T>(bwd24_kernel<PHASE, bf16_t, float, SAVED, ADAMW, T>, a, np, s, c);
     if (g_dt == MASKGS_BF16)
-        return go(bwd24_kernel<PHASE, float, bf16_t, SAVED, ADAMW>, a, np, s, c);
-    return go(bwd24_kernel<PHASE, float, float, SAVED, ADAMW>, a, np, s, c);
+        return go<T>(bwd24_kernel<PHASE, float, bf16_t, SAVED, ADAMW, T>, a, np, s, c);
+    return go<T>(bwd24_kernel<PHASE, float, float, SAVED, ADAMW, T>, a, np, s, c);
 }
 
 template <bool ADAMW>
