@@ -39,10 +39,16 @@ constexpr int kWgPerCUStream = 64;
 // again (without the fused update): 1024-lane workgroups, one resident per CU
 // (72 KB of LDS, 75 registers), took the 7B step's backward phase from 18.8
 // to 18.3 ms against 512-lane ones (grid caps of 2, 4 and 8 per CU within
-// 0.5% of each other).  The forward measured within 1% of 512 lanes at 256
-// and 768, and keeps kThreads.
+// 0.5% of each other).
 constexpr int kBwdRcThreads = 1024;
 constexpr int kBwdRcWgPerCU = 4;
+// The same for the forward that saves no soft index (the step's forward):
+// 768-lane workgroups, 2 per CU, both resident (24 waves), 13.51 -> 13.31 ms
+// over the 7B step's forward phase in three alternating runs against 512
+// lanes and 8 per CU (256 lanes and 8 per CU: 13.38; 384 and 1024 lanes:
+// 14.3-14.4).
+constexpr int kFwdNoYThreads = 768;
+constexpr int kFwdNoYWgPerCU = 2;
 using C24 = Cands<2, 4>;
 
 // ---------------------------------------------------------------------------
@@ -492,8 +498,9 @@ __device__ __forceinline__ void applied_mask4(const float *y6, uint32_t hm, bool
 }
 
 // Workgroup sum of one double per lane, added atomically to *dst.
+template <int T = kThreads>
 __device__ __forceinline__ void reduce_add(double v, double *dst) {
-    __shared__ double part[kThreads / 64];
+    __shared__ double part[T / 64];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -502,7 +509,7 @@ __device__ __forceinline__ void reduce_add(double v, double *dst) {
     if (threadIdx.x == 0) {
         double s = 0.0;
 #pragma unroll
-        for (int i = 0; i < kThreads / 64; ++i) s += part[i];
+        for (int i = 0; i < T / 64; ++i) s += part[i];
         atomicAdd(dst, s);
     }
 }
@@ -510,17 +517,17 @@ __device__ __forceinline__ void reduce_add(double v, double *dst) {
 // ---------------------------------------------------------------------------
 // Forward: W (.) M~, optional soft index and regulariser value.
 // ---------------------------------------------------------------------------
-template <int PHASE, typename WT, typename OT, bool YSAVE>
-__global__ __launch_bounds__(kThreads) void fwd24_kernel(FwdArgs a) {
-    __shared__ float4 stage[YSAVE ? 3 * kThreads : 1];
+template <int PHASE, typename WT, typename OT, bool YSAVE, int T>
+__global__ __launch_bounds__(T) void fwd24_kernel(FwdArgs a) {
+    __shared__ float4 stage[YSAVE ? 3 * T : 1];
     __shared__ float4 gtab[kGumbelRows];
-    load_gumbel_table<kThreads>(gtab);
+    load_gumbel_table<T>(gtab);
     __syncthreads();
     const bool hard = a.idx || a.bits || a.values || a.val_idx;
     const int64_t npairs = (a.g.nblocks + 1) >> 1;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * T;
     double reg = 0.0;
-    for (int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads; base < npairs;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * T; base < npairs;
          base += stride) {
         const int64_t p = base + threadIdx.x;
         float y[12];
@@ -555,7 +562,7 @@ __global__ __launch_bounds__(kThreads) void fwd24_kernel(FwdArgs a) {
         }
         if constexpr (YSAVE) store12_wave(a.y, base, a.g.nblocks, y, stage);
     }
-    if (a.reg) reduce_add(reg, a.reg);
+    if (a.reg) reduce_add<T>(reg, a.reg);
 }
 
 // ---------------------------------------------------------------------------
@@ -960,13 +967,15 @@ template <int PHASE, bool YSAVE>
 hipError_t fwd24_dispatch(const FwdArgs &a, maskgs_dtype w_dt, maskgs_dtype o_dt,
                           hipStream_t s) {
     const int64_t np = (a.g.nblocks + 1) >> 1;
+    constexpr int T = YSAVE ? kThreads : kFwdNoYThreads;
+    const int c = YSAVE ? kWgPerCU : kFwdNoYWgPerCU;
     if (w_dt == MASKGS_BF16 && o_dt == MASKGS_BF16)
-        return go(fwd24_kernel<PHASE, bf16_t, bf16_t, YSAVE>, a, np, s);
+        return go<T>(fwd24_kernel<PHASE, bf16_t, bf16_t, YSAVE, T>, a, np, s, c);
     if (w_dt == MASKGS_BF16 && o_dt == MASKGS_F32)
-        return go(fwd24_kernel<PHASE, bf16_t, float, YSAVE>, a, np, s);
+        return go<T>(fwd24_kernel<PHASE, bf16_t, float, YSAVE, T>, a, np, s, c);
     if (w_dt == MASKGS_F32 && o_dt == MASKGS_BF16)
-        return go(fwd24_kernel<PHASE, float, bf16_t, YSAVE>, a, np, s);
-    return go(fwd24_kernel<PHASE, float, float, YSAVE>, a, np, s);
+        return go<T>(fwd24_kernel<PHASE, float, bf16_t, YSAVE, T>, a, np, s, c);
+    return go<T>(fwd24_kernel<PHASE, float, float, YSAVE, T>, a, np, s, c);
 }
 
 template <int PHASE, bool SAVED, bool ADAMW>
