@@ -21,7 +21,11 @@
 namespace maskgs {
 namespace {
 
-constexpr int kThreads = 256;
+// Lanes per workgroup: 512 against 256 took the 7B sweep's draw 10.44 -> 10.22
+// ms, the gradient from the saved order 9.04 -> 8.88 ms and the redrawn one
+// 10.31 -> 10.07 ms (three alternating runs), with half as many copies of the
+// noise table to load.
+constexpr int kThreads = 512;
 
 // ---------------------------------------------------------------------------
 // Vector access to one block of M elements of T.
@@ -429,7 +433,7 @@ __global__ __launch_bounds__(kThreads) void mp_init_kernel(MpInitArgs a) {
         mp_init_block<N, M, WT>(a, b);
 }
 
-// One thread per block up to 2^20 workgroups (2.7e8 blocks); larger tensors
+// One thread per block up to 2^20 workgroups (5.4e8 blocks); larger tensors
 // loop, which keeps the grid inside its 32-bit dimension.
 unsigned blocks_for(int64_t nblocks) {
     const int64_t want = (nblocks + kThreads - 1) / kThreads;
@@ -437,10 +441,10 @@ unsigned blocks_for(int64_t nblocks) {
 }
 
 // The kernels that draw noise first copy the 24 KB coefficient table into
-// LDS, so their grids stop at the workgroups that fit the CUs at once (six of
-// 256 lanes per CU by LDS) and loop over the rest: the table is read once per
-// resident workgroup instead of once per 256 blocks.
-constexpr int kNoiseWgPerCU = 6;
+// LDS, so their grids stop at the workgroups that fit the CUs at once (three
+// of 512 lanes per CU by registers) and loop over the rest: the table is read
+// once per resident workgroup instead of once per 512 blocks.
+constexpr int kNoiseWgPerCU = 3;
 unsigned noise_blocks_for(int64_t nblocks) {
     const int64_t want = (nblocks + kThreads - 1) / kThreads;
     const int64_t cap = static_cast<int64_t>(device_cu_count()) * kNoiseWgPerCU;

@@ -12,7 +12,7 @@ Bars:
     kernel forms with a few roundings (exp, the sum Z of at most M terms, the
     reciprocal, the product); the error of dlogp measured at most 4.6e-7 of
     its unit scale, within the 1e-6 absolute bound, and A scales it.
-Small shapes in full (several 256-block workgroups and a ragged tail, odd and
+Small shapes in full (several workgroups and a ragged tail, odd and
 even global block offsets), the draw's Plackett-Luce frequencies, then one
 full-size tensor per pattern on sampled rows.
 """
