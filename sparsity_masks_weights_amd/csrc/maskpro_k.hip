@@ -7,8 +7,10 @@
 // One lane per block.  A block's logits are 16 B (2:4) or 32 B (4:8) and its
 // weights 8 or 16 B (bf16), so consecutive lanes read consecutive 16-byte
 // vectors: every load and store is a coalesced dwordx2/dwordx4.  There is no
-// reuse between blocks, hence no LDS; the work per byte is the Philox stream
-// and two logarithms per position, which keeps the draw near the VALU/HBM
+// reuse between blocks; LDS holds only the noise contract's coefficient
+// table, one copy per workgroup.  The work per byte is the Philox stream and
+// one table evaluation per position (and, for the gradient drawn again, the
+// N rounds of exponentials), which keeps these kernels near the VALU/HBM
 // balance point.
 #include <hip/hip_runtime.h>
 
