@@ -801,8 +801,8 @@ def host_array(t, shape=None):
 
 def cpu_baseline(wl, bufs, min_secs=10.0):
     """The CPU oracle (all host threads) on whole tensors of the workload, in
-    order (starting over after the last one), until at least `min_secs` of
-    CPU work: fwd + bwd + hard extract."""
+    order (starting over after the last one), until the oracle has run for at
+    least `min_secs` of wall time: fwd + bwd + hard extract."""
     import itertools
     import numpy as np
     import torch
@@ -836,12 +836,13 @@ def cpu_baseline(wl, bufs, min_secs=10.0):
     return {"value": round(blocks / secs, 1), "unit": "weight-blocks/s", "cores": used,
             "kind": "oracle", "host": host_cpu(),
             "sample": f"{what} ({blocks} blocks): fwd + bwd + hard extract, {secs:.1f} s of "
-                      f"CPU time"}
+                      f"oracle wall time on {used} threads"}
 
 
 def cpu_baseline_linear(wl, bufs, mp_bufs, min_secs=8.0):
     """The CPU oracle of the linear-space variant (all host threads) on whole
-    tensors of the workload, in order, until at least `min_secs` of CPU work:
+    tensors of the workload, in order, until the oracle has run for at least
+    `min_secs` of wall time:
     draw + masked weights, then the policy gradient of the saved draw order."""
     import oracle
 
@@ -866,7 +867,8 @@ def cpu_baseline_linear(wl, bufs, mp_bufs, min_secs=8.0):
     return {"value": round(blocks / secs, 1), "unit": "weight-blocks/s", "cores": used,
             "kind": "oracle", "host": host_cpu(),
             "sample": f"first {tensors} tensor(s) of the same workload ({blocks} blocks): draw + "
-                      f"masked weights + policy gradient, {secs:.1f} s of CPU time"}
+                      f"masked weights + policy gradient, {secs:.1f} s of oracle wall time on "
+                      f"{used} threads"}
 
 
 def run_profile(mg, wl, args, dev):
