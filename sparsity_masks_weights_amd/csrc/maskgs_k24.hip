@@ -33,7 +33,8 @@ constexpr int kWgPerCU = MASKGS_K24_WG_PER_CU;  // grid cap: workgroups of kThre
 // resident set keeps each workgroup's share, and so the launch's tail, short.
 // Measured on the 7B sweep against the cap of 8: hard extract 11.4 -> 10.7 ms,
 // prior seeding 16.8 -> 15.8 ms, training backward 46.8 -> 45.6 ms; the
-// forward and the plain backward measured best at 8.
+// 512-lane forward and backward measured best at 8 (the step's two kernels
+// use the shapes below).
 constexpr int kWgPerCUStream = 64;
 // Lanes per workgroup and grid cap of the backward that draws the soft index
 // again (without the fused update): 1024-lane workgroups, one resident per CU
