@@ -379,16 +379,18 @@ class Session:
             # the VALU side of the same launch: its wave-level VALU instruction
             # count (rocprofv3 SQ_INSTS_VALU) over the launch time measured here
             pairs = recorded(VALU_FILE, wl.key, kind, d["B"], "valu_dual_issued_per_launch") or 0
+            trans = recorded(VALU_FILE, wl.key, kind, d["B"], "valu_trans_per_launch") or 0
             rate = insts / (ms * 1e3)
             # SIMD issue time the instructions need: 2 cycles per dual-issued
-            # instruction, 4 per other one, over the launch's SIMD cycles
-            need = (2 * pairs + 4 * (insts - pairs)) / (256 * 4 * 2.4e9)
+            # instruction, 8 per fp32 transcendental, 4 per other one, over the
+            # launch's SIMD cycles
+            need = (2 * pairs + 8 * trans + 4 * (insts - pairs - trans)) / (256 * 4 * 2.4e9)
             roof["valu"] = dict(achieved=round(rate, 1), peak=VALU_PEAK_DUAL,
                                 single_issue_peak=VALU_PEAK_SINGLE,
                                 unit="wave instructions/us", frac=round(rate / VALU_PEAK_DUAL, 4),
                                 dual_issued_frac=round(pairs / insts, 4),
                                 issue_time_frac=round(need / (ms * 1e-3), 4),
-                                insts_per_launch=int(insts))
+                                insts_per_launch=int(insts), trans_insts_per_launch=int(trans))
         return roof
 
 
