@@ -246,7 +246,8 @@ class Session:
     def ev(self):
         return self.torch.cuda.Event(enable_timing=True)
 
-    def run_phase(self, kind, tensors, timed=-1, pref=None, record=True, fn=None):
+    def run_phase(self, kind, tensors, timed=-1, pref=None, record=True, fn=None,
+                  phase_events=True):
         """Launches `kind` (or fn(buffers, stream, index)) on every tensor
         index in `tensors`, alternating between the worker streams, between
         phase events on the main stream.  Launch number `timed` (on a largest
@@ -254,10 +255,13 @@ class Session:
         which first waits for the other workers' queued work, and they wait
         for it; so its events time the kernel by itself and not its overlap
         with a neighbour, and its start event directly follows a kernel in
-        order."""
+        order.  Without phase_events (or record) the phase records no timing
+        events of its own."""
         nw = len(self.workers)
+        phase_events = phase_events and record
         p0, p1 = self.ev(), self.ev()
-        p0.record(self.stream)
+        if phase_events:
+            p0.record(self.stream)
         if len(tensors) == 1:
             # one launch: nothing to overlap, so it runs on the main stream
             i = tensors[0]
@@ -271,8 +275,8 @@ class Session:
             if timed == 0:
                 e1.record(self.stream)
                 self.launch_ev.setdefault(kind, []).append((e0, e1))
-            p1.record(self.stream)
-            if record:
+            if phase_events:
+                p1.record(self.stream)
                 self.phase.setdefault(kind, []).append((p0, p1))
             return
         self.fork()
@@ -298,18 +302,20 @@ class Session:
                     o.wait_event(e1)
                 self.launch_ev.setdefault(kind, []).append((e0, e1))
         self.join()
-        p1.record(self.stream)
-        if record:
+        if phase_events:
+            p1.record(self.stream)
             self.phase.setdefault(kind, []).append((p0, p1))
 
-    def timed_steps(self, kinds, nsteps, warmup, timed_kind=None, schedule=None):
+    def timed_steps(self, kinds, nsteps, warmup, timed_kind=None, schedule=None,
+                    phase_events=True):
         """`warmup` untimed then `nsteps` timed steps of `kinds`; returns ms
         per timed step.  Copy c of the buffers serves steps c, c + copies, ...
         schedule(s) sets the sampling parameters of step s (default: the
         step number only).  Per-launch events bracket one launch of
         `timed_kind` on a largest tensor per timed step, spread evenly over
         those tensors; a timed launch runs alone, which costs the step the
-        overlap on both sides of it."""
+        overlap on both sides of it.  phase_events: time every phase too
+        (each timing event costs the stream a few microseconds)."""
         torch = self.torch
 
         def one(s, timed_launch):
@@ -326,7 +332,8 @@ class Session:
                 if kind == timed_kind and timed_launch and bigs:
                     stride = max(1, len(bigs) // nsteps)
                     t = bigs[(s * stride) % len(bigs)]
-                self.run_phase(kind, tensors, t, record=timed_launch)
+                self.run_phase(kind, tensors, t, record=timed_launch,
+                               phase_events=phase_events)
 
         for s in range(warmup):
             one(s, False)
@@ -341,6 +348,20 @@ class Session:
         t1.record(self.stream)
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / nsteps
+
+    def measure(self, kinds, nsteps, timed_kind=None, schedule=None, warmup=0,
+                breakdown_steps=3):
+        """The timed steps without per-phase events (ms per step, and the
+        roofline of `timed_kind` from its per-launch events), then
+        `breakdown_steps` further steps with phase events for the per-kernel
+        breakdown: each timing event costs the stream a few microseconds,
+        a fifth of a single-tensor step's time."""
+        ms = self.timed_steps(kinds, nsteps, warmup, timed_kind=timed_kind, schedule=schedule,
+                              phase_events=False)
+        roof = self.roofline(timed_kind) if timed_kind else None
+        nb = max(1, min(nsteps, breakdown_steps))
+        self.timed_steps(kinds, nb, 0, schedule=schedule)
+        return ms, self.kernel_stats(kinds, nb), roof
 
     def phase_ms(self, kind, nsteps):
         return sum(a.elapsed_time(b) for a, b in self.phase.get(kind, [])) / nsteps
@@ -471,25 +492,25 @@ def run_main(mg, wl, specs, args, dev, extras=True, cpu_secs=10.0):
     # largest tensor is timed alone in each timed step
     sess.timed_steps(kinds, 1, max(1, args.warmup))
     dom = sess.dominant(kinds)
-    ms_step = sess.timed_steps(kinds, args.steps, 0, timed_kind=dom)
+    ms_step, kern, roof = sess.measure(kinds, args.steps, timed_kind=dom)
     result = line(sess, ms_step, kinds, args.steps, args, mode)
-    result["kernels"] = sess.kernel_stats(kinds, args.steps)
-    result["roofline"] = sess.roofline(dom)
+    result["kernels"] = kern
+    result["roofline"] = roof
     # the other design of the step, for comparison
     other = "saved" if mode == "recompute" else "recompute"
     okinds = step_kinds(other)
-    ms_o = sess.timed_steps(okinds, args.steps, 1)
+    ms_o, kern_o, _ = sess.measure(okinds, args.steps, warmup=1)
     result["other_step"] = dict(step_mode=other, what=describe_step(other),
                                 ms_per_step=round(ms_o, 3),
                                 value=round(sess.blocks / (ms_o * 1e-3), 1),
-                                kernels=sess.kernel_stats(okinds, args.steps))
+                                kernels=kern_o)
     if extras:
         ukinds = ("fwd", "bwd", "hard")
-        ms_u = sess.timed_steps(ukinds, args.steps, 0)
+        ms_u, kern_u, _ = sess.measure(ukinds, args.steps)
         result["unfused_step"] = dict(
             order="fwd, bwd, then hard extract (separate pass over z and W)",
             ms_per_step=round(ms_u, 3), value=round(sess.blocks / (ms_u * 1e-3), 1),
-            kernels=sess.kernel_stats(ukinds, args.steps))
+            kernels=kern_u)
         result.update(extra_sections(mg, sess, args))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, sess.bufs[:sess.per_copy], min_secs=cpu_secs)
@@ -706,14 +727,14 @@ def run_qproj_prior(mg, args, dev):
     sess.timed_steps(kinds, 1, max(1, args.warmup))
     dom = sess.dominant(kinds)
     nsteps = copies * max(1, args.steps // copies)
-    ms = sess.timed_steps(kinds, nsteps, 0, timed_kind=dom)
+    ms, kern, roof = sess.measure(kinds, nsteps, timed_kind=dom)
     res = line(sess, ms, kinds, nsteps, args, mode, {
         "logits": f"fp32 N(0,{wl.z_std}) seeded by the magnitude top-2 prior, alpha "
                   f"{wl.prior_alpha}",
         "buffer_rotation": f"{copies} copies, step s uses copy s mod {copies}; "
                            f"{copy_traffic / 1e6:.0f} MB of step traffic per copy"})
-    res["kernels"] = sess.kernel_stats(kinds, nsteps)
-    res["roofline"] = sess.roofline(dom)
+    res["kernels"] = kern
+    res["roofline"] = roof
     res["prior_init"] = {"ms_per_tensor": round(e0.elapsed_time(e1) / copies, 4)}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, sess.bufs[:1], min_secs=5.0)
@@ -738,13 +759,13 @@ def run_mlp_anneal(mg, args, dev):
     sess.timed_steps(kinds, 1, max(1, args.warmup), schedule=sched)
     dom = sess.dominant(kinds)
     nsteps = wl.steps * max(1, args.steps // wl.steps)
-    ms = sess.timed_steps(kinds, nsteps, 0, timed_kind=dom, schedule=sched)
+    ms, kern, roof = sess.measure(kinds, nsteps, timed_kind=dom, schedule=sched)
     res = line(sess, ms, kinds, nsteps, args, mode, {
         "kappa": f"{wl.kappa} -> {wl.kappa_end}", "tau": f"{wl.tau} -> {wl.tau_end}",
         "schedule": f"linear over {wl.steps} steps (both ends included), the anneal repeated "
                     f"{nsteps // wl.steps}x"})
-    res["kernels"] = sess.kernel_stats(kinds, nsteps)
-    res["roofline"] = sess.roofline(dom)
+    res["kernels"] = kern
+    res["roofline"] = roof
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, sess.bufs, min_secs=5.0)
     return res
